@@ -1,0 +1,200 @@
+"""Exact disentangled (C2P/P2C) self-attention on AMD gfx950.
+
+A thin ctypes binding of ``libdf_attn.so`` (declared in ``include/df_attn.h``).
+It only marshals arguments: every step of the computation runs in the HIP
+kernels of the library. PyTorch supplies device memory and the current
+stream. If the library is missing, every call raises; there is no fallback.
+
+Layouts: ``q, k, v, out, dout`` and their gradients are ``[T, H, D]`` (packed,
+with ``cu_seqlens``) or ``[B, L, H, D]`` (padded); ``q_r, k_r`` are
+``[H, R, D]``; ``lse`` is float32 ``[H, T]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "bwd",
+           "DfError", "DTYPE_CODES", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
+DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+
+EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
+            "df_attn_fwd", "df_attn_bwd", "df_strerror", "df_last_error", "df_attn_version")
+
+
+class DfError(RuntimeError):
+    """An error code returned by the library."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"df_attn error {code}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m deberta_disentangled_attention_rel_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sp = ctypes.POINTER(Shape)
+    L.df_attn_supported.argtypes = [sp, i32, i32]
+    L.df_attn_supported.restype = ctypes.c_int
+    L.df_attn_workspace_size.argtypes = [ctypes.c_int, sp, i32, i32]
+    L.df_attn_workspace_size.restype = sz
+    L.df_build_rel_index.argtypes = [i32, i32, i32, vp, vp, vp]
+    L.df_build_rel_index.restype = ctypes.c_int
+    L.df_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.df_attn_fwd.restype = ctypes.c_int
+    L.df_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
+                              vp, vp, vp, vp, vp, vp, sz, vp]
+    L.df_attn_bwd.restype = ctypes.c_int
+    L.df_strerror.argtypes = [ctypes.c_int]
+    L.df_strerror.restype = ctypes.c_char_p
+    L.df_last_error.argtypes = []
+    L.df_last_error.restype = ctypes.c_char_p
+    L.df_attn_version.argtypes = []
+    L.df_attn_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        L = lib()
+        raise DfError(rc, f"{L.df_strerror(rc).decode()}: {L.df_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_thd(x: torch.Tensor) -> torch.Tensor:
+    """View ``[B, L, H, D]`` as ``[B*L, H, D]`` (no copy when possible)."""
+    if x.dim() == 4:
+        return x.reshape(x.shape[0] * x.shape[1], x.shape[2], x.shape[3])
+    if x.dim() != 3:
+        raise ValueError(f"expected [T,H,D] or [B,L,H,D], got {tuple(x.shape)}")
+    return x
+
+
+def make_shape(q: torch.Tensor, batch: int, max_seqlen: int) -> Shape:
+    T, H, D = q.shape
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return Shape(int(batch), int(max_seqlen), int(T), int(H), int(D), DTYPE_CODES[q.dtype],
+                 int(q.stride(0)), int(q.stride(1)))
+
+
+def _layout(q, k, v, cu_seqlens, max_seqlen):
+    """Common shape marshalling of fwd/bwd: returns ([T,H,D] views, batch, L)."""
+    padded4 = q.dim() == 4
+    if cu_seqlens is not None:
+        if max_seqlen is None:
+            raise ValueError("packed layout needs max_seqlen")
+        batch, L = cu_seqlens.numel() - 1, int(max_seqlen)
+    elif padded4:
+        batch, L = q.shape[0], q.shape[1]
+    else:
+        if max_seqlen is None:
+            raise ValueError("[T,H,D] without cu_seqlens needs max_seqlen (= L)")
+        L = int(max_seqlen)
+        batch = q.shape[0] // L
+    q3, k3, v3 = (_as_thd(x).contiguous() for x in (q, k, v))
+    return q3, k3, v3, batch, L
+
+
+def build_rel_index(max_seqlen: int, span: int, buckets: int, device="cuda"):
+    """The two relative-index tables (int32, ``2*max_seqlen - 1`` entries)."""
+    n = 2 * int(max_seqlen) - 1
+    c2p = torch.empty(n, dtype=torch.int32, device=device)
+    p2c = torch.empty(n, dtype=torch.int32, device=device)
+    _check(lib().df_build_rel_index(int(max_seqlen), int(span), int(buckets), _ptr(c2p), _ptr(p2c),
+                                    _stream(c2p.device)))
+    return c2p, p2c
+
+
+def workspace_size(pass_: int, shape: Shape, span: int, buckets: int) -> int:
+    return int(lib().df_attn_workspace_size(int(pass_), ctypes.byref(shape), int(span), int(buckets)))
+
+
+def supported(shape: Shape, span: int, buckets: int) -> int:
+    """0 if the configuration is accepted, else the error code (non-raising)."""
+    return int(lib().df_attn_supported(ctypes.byref(shape), int(span), int(buckets)))
+
+
+def _workspace(pass_, shape, span, buckets, device, workspace):
+    need = workspace_size(pass_, shape, span, buckets)
+    if need == 0:
+        _check(supported(shape, span, buckets))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=None,
+        max_seqlen: Optional[int] = None, out=None, lse=None, workspace=None):
+    """Forward pass. Returns ``(out, lse)`` with ``out`` shaped like ``q``."""
+    q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    shape = make_shape(q3, batch, L)
+    T, H, D = q3.shape
+    if out is None:
+        out = torch.empty_like(q3)
+    out3 = _as_thd(out)
+    if out3.shape != q3.shape or not out3.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    ws = _workspace(0, shape, span, buckets, q.device, workspace)
+    q_r, k_r = q_r.contiguous(), k_r.contiguous()
+    _check(lib().df_attn_fwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
+                             int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
+                             _ptr(out3), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out.view(q.shape) if q.dim() == 4 else out, lse
+
+
+def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=None,
+        cu_seqlens=None, max_seqlen: Optional[int] = None, grads=None, workspace=None):
+    """Backward pass. Returns ``(dq, dk, dv, dq_r, dk_r)``."""
+    q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    shape = make_shape(q3, batch, L)
+    out3, dout3 = _as_thd(out).contiguous(), _as_thd(dout).contiguous()
+    if grads is None:
+        grads = (torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3),
+                 torch.empty_like(q_r), torch.empty_like(k_r))
+    dq, dk, dv, dq_r, dk_r = grads
+    for g_ in (dq, dk, dv):
+        if _as_thd(g_).shape != q3.shape or not g_.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors shaped like q")
+    ws = _workspace(1, shape, span, buckets, q.device, workspace)
+    q_r, k_r = q_r.contiguous(), k_r.contiguous()
+    _check(lib().df_attn_bwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
+                             int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
+                             _ptr(out3), _ptr(lse), _ptr(dout3), _ptr(_as_thd(dq)), _ptr(_as_thd(dk)),
+                             _ptr(_as_thd(dv)), _ptr(dq_r), _ptr(dk_r), _ptr(ws), ws.numel(),
+                             _stream(q.device)))
+    if q.dim() == 4:
+        dq, dk, dv = (x.view(q.shape) for x in (dq, dk, dv))
+    return dq, dk, dv, dq_r, dk_r

@@ -1,0 +1,317 @@
+// C ABI of the library: argument validation, workspace planning and launch
+// sequencing. Validation is pure host code and runs before any HIP call.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "df_attn.h"
+#include "params.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DF_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t dtype_size(int dt) { return dt == DF_FP32 ? 4 : 2; }
+
+int index_params(int32_t span, int32_t buckets, int* att, int* R) {
+  if (span < 1) return fail(DF_ERR_INVALID, "span (max_relative_positions) must be >= 1, got %d", span);
+  if (buckets < 0) return fail(DF_ERR_INVALID, "buckets must be >= 0, got %d", buckets);
+  if (buckets > 0) {
+    if (buckets < 2) return fail(DF_ERR_INVALID, "buckets must be 0 or >= 2, got %d", buckets);
+    if (!(span - 1 > buckets / 2))
+      return fail(DF_ERR_INVALID,
+                  "log buckets need span - 1 > buckets / 2 (span %d, buckets %d)", span, buckets);
+  }
+  const long a = buckets > 0 ? buckets : span;
+  if (2 * a > (1 << 20)) return fail(DF_ERR_INVALID, "relative rows 2*att = %ld too large", 2 * a);
+  *att = int(a);
+  *R = int(2 * a);
+  return DF_OK;
+}
+
+int check_shape(const df_attn_shape* s) {
+  if (!s) return fail(DF_ERR_INVALID, "shape is NULL");
+  if (s->dtype != DF_BF16 && s->dtype != DF_FP16 && s->dtype != DF_FP32)
+    return fail(DF_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+  if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
+    return fail(DF_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128, got %d", s->head_dim);
+  if (s->batch < 1) return fail(DF_ERR_INVALID, "batch must be >= 1, got %d", s->batch);
+  if (s->max_seqlen < 1 || s->max_seqlen > (1 << 24))
+    return fail(DF_ERR_INVALID, "max_seqlen must be in [1, 2^24], got %d", s->max_seqlen);
+  if (s->num_heads < 1 || s->num_heads > 65535)
+    return fail(DF_ERR_INVALID, "num_heads must be in [1, 65535], got %d", s->num_heads);
+  if (s->total_tokens < 0) return fail(DF_ERR_INVALID, "total_tokens must be >= 0");
+  if (s->total_tokens > (int64_t(1) << 40)) return fail(DF_ERR_INVALID, "total_tokens too large");
+  const int64_t D = s->head_dim, H = s->num_heads, T = s->total_tokens;
+  const int64_t vec = s->dtype == DF_FP32 ? 4 : 8;
+  if (s->tok_stride <= 0 || s->head_stride <= 0)
+    return fail(DF_ERR_INVALID, "strides must be positive (tok %lld, head %lld)",
+                (long long)s->tok_stride, (long long)s->head_stride);
+  if (s->tok_stride % vec || s->head_stride % vec)
+    return fail(DF_ERR_INVALID, "strides must be multiples of %lld elements", (long long)vec);
+  // rows of distinct (token, head) pairs must not overlap: token-major
+  // ([T,H,D]-like) or head-major ([H,T,D]-like) placement
+  const bool tok_major = s->head_stride >= D && s->tok_stride >= (H - 1) * s->head_stride + D;
+  const bool head_major = s->tok_stride >= D && s->head_stride >= (T > 0 ? T - 1 : 0) * s->tok_stride + D;
+  if (!tok_major && !head_major)
+    return fail(DF_ERR_INVALID, "strides (tok %lld, head %lld) make rows overlap",
+                (long long)s->tok_stride, (long long)s->head_stride);
+  return DF_OK;
+}
+
+int check_all(const df_attn_shape* s, int32_t span, int32_t buckets, bool packed, int* att, int* R) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = index_params(span, buckets, att, R);
+  if (rc) return rc;
+  if (!packed && int64_t(s->batch) * s->max_seqlen != s->total_tokens)
+    return fail(DF_ERR_INVALID, "padded layout needs total_tokens == batch*max_seqlen (%lld != %d*%d)",
+                (long long)s->total_tokens, s->batch, s->max_seqlen);
+  return DF_OK;
+}
+
+// Workspace plan. Offsets are relative to the workspace base.
+struct Plan {
+  size_t lut, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
+  int RP, nchunk, chunk_tokens;
+};
+
+Plan make_plan(int pass, const df_attn_shape* s, int R) {
+  Plan pl{};
+  const size_t es = dtype_size(s->dtype);
+  const size_t T = size_t(s->total_tokens), H = size_t(s->num_heads), D = size_t(s->head_dim);
+  pl.RP = int((R + 7) / 8 * 8);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  pl.lut = take(2 * (2 * size_t(s->max_seqlen) - 1) * sizeof(int32_t));
+  pl.c2ps = take(H * T * pl.RP * es);
+  pl.p2cs = take(H * T * pl.RP * es);
+  pl.ends = take(4 * H * T * es);
+  if (pass == 1) {
+    // split-K over tokens for the [R, D] weight gradients: about 512
+    // workgroups, chunk length a multiple of 32 tokens; a function of the
+    // shape only, so the summation order is fixed
+    const int64_t rtiles = (R + 127) / 128;
+    int64_t nchunk = (512 + int64_t(H) * rtiles - 1) / (int64_t(H) * rtiles);
+    const int64_t maxc = (int64_t(T) + 31) / 32;
+    if (nchunk > maxc) nchunk = maxc;
+    if (nchunk < 1) nchunk = 1;
+    int64_t ct = (int64_t(T) + nchunk - 1) / nchunk;
+    ct = (ct + 31) / 32 * 32;
+    if (ct < 32) ct = 32;
+    nchunk = T > 0 ? (int64_t(T) + ct - 1) / ct : 0;
+    pl.nchunk = int(nchunk);
+    pl.chunk_tokens = int(ct);
+    pl.delta = take(H * T * sizeof(float));
+    pl.dq_acc = take(H * T * D * sizeof(float));
+    pl.dk_acc = take(H * T * D * sizeof(float));
+    pl.dc2p = take(H * T * pl.RP * es);
+    pl.dp2c = take(H * T * pl.RP * es);
+    pl.part = take(2 * H * size_t(nchunk) * size_t(R) * D * sizeof(float));
+  }
+  pl.total = o;
+  return pl;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int check_ptr(const void* ptr, const char* name, size_t al) {
+  if (!ptr) return fail(DF_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(ptr, al)) return fail(DF_ERR_INVALID, "%s must be %zu-byte aligned", name, al);
+  return DF_OK;
+}
+
+dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, int att, int R,
+                        const Plan& pl, char* ws, const uint8_t* key_mask, const int32_t* cu) {
+  dfa::Params p{};
+  p.nseq = s->batch;
+  p.Lmax = s->max_seqlen;
+  p.H = s->num_heads;
+  p.D = s->head_dim;
+  p.R = R;
+  p.RP = pl.RP;
+  p.att = att;
+  p.span = span;
+  p.buckets = buckets;
+  p.dtype = s->dtype;
+  p.T = s->total_tokens;
+  p.ts = s->tok_stride;
+  p.hs = s->head_stride;
+  p.cu = cu;
+  p.kmask = key_mask;
+  p.scale = float(1.0 / std::sqrt(3.0 * s->head_dim));
+  p.scale_log2 = float(1.4426950408889634 / std::sqrt(3.0 * s->head_dim));
+  p.c2p = reinterpret_cast<int32_t*>(ws + pl.lut);
+  p.p2c = p.c2p + (2 * size_t(s->max_seqlen) - 1);
+  p.c2ps = ws + pl.c2ps;
+  p.p2cs = ws + pl.p2cs;
+  p.ends = ws + pl.ends;
+  p.nchunk = pl.nchunk;
+  p.chunk_tokens = pl.chunk_tokens;
+  return p;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int df_attn_version(void) { return 100; }
+
+const char* df_strerror(int code) {
+  switch (code) {
+    case DF_OK: return "ok";
+    case DF_ERR_INVALID: return "invalid argument";
+    case DF_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DF_ERR_WORKSPACE: return "workspace too small";
+    case DF_ERR_HIP: return "HIP error";
+    default: return "unknown error";
+  }
+}
+
+const char* df_last_error(void) { return g_last_error.c_str(); }
+
+int df_attn_supported(const df_attn_shape* shape, int32_t span, int32_t buckets) {
+  int att, R;
+  const int rc = check_all(shape, span, buckets, /*packed=*/true, &att, &R);
+  return rc ? rc : ok();
+}
+
+size_t df_attn_workspace_size(int pass, const df_attn_shape* shape, int32_t span, int32_t buckets) {
+  int att, R;
+  if (pass != 0 && pass != 1) return 0;
+  if (check_all(shape, span, buckets, true, &att, &R)) return 0;
+  return make_plan(pass, shape, R).total;
+}
+
+int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets, int32_t* c2p_lut,
+                       int32_t* p2c_lut, void* stream) {
+  int att, R;
+  if (max_seqlen < 1 || max_seqlen > (1 << 24))
+    return fail(DF_ERR_INVALID, "max_seqlen must be in [1, 2^24], got %d", max_seqlen);
+  int rc = index_params(span, buckets, &att, &R);
+  if (rc) return rc;
+  if (!c2p_lut || !p2c_lut) return fail(DF_ERR_INVALID, "table pointers must not be NULL");
+  rc = hip_check(dfa::launch_lut(max_seqlen, span, buckets, c2p_lut, p2c_lut, (hipStream_t)stream),
+                 "relative index kernel");
+  return rc ? rc : ok();
+}
+
+int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens, void* out, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int att, R;
+  int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q", 16)) || (rc = check_ptr(k, "k", 16)) || (rc = check_ptr(v, "v", 16)) ||
+      (rc = check_ptr(q_r, "q_r", 16)) || (rc = check_ptr(k_r, "k_r", 16)) ||
+      (rc = check_ptr(out, "out", 16)) || (rc = check_ptr(lse, "lse", 4)))
+    return rc;
+  const Plan pl = make_plan(0, shape, R);
+  if (workspace_bytes < pl.total)
+    return fail(DF_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+  if ((rc = check_ptr(workspace, "workspace", kAlign))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  dfa::Params p = base_params(shape, span, buckets, att, R, pl, (char*)workspace, key_mask, cu_seqlens);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qr = q_r;
+  p.kr = k_r;
+  p.out = out;
+  p.lse = lse;
+  if (p.T == 0) return ok();
+  if ((rc = hip_check(dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st), "relative index kernel")))
+    return rc;
+  if ((rc = hip_check(dfa::launch_strips(p, st), "strip kernel"))) return rc;
+  if ((rc = hip_check(dfa::launch_fwd(p, st), "forward kernel"))) return rc;
+  return ok();
+}
+
+int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens, const void* out, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int att, R;
+  int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
+  if (rc) return rc;
+  if ((rc = check_ptr(q, "q", 16)) || (rc = check_ptr(k, "k", 16)) || (rc = check_ptr(v, "v", 16)) ||
+      (rc = check_ptr(q_r, "q_r", 16)) || (rc = check_ptr(k_r, "k_r", 16)) ||
+      (rc = check_ptr(out, "out", 16)) || (rc = check_ptr(lse, "lse", 4)) ||
+      (rc = check_ptr(dout, "dout", 16)) || (rc = check_ptr(dq, "dq", 16)) ||
+      (rc = check_ptr(dk, "dk", 16)) || (rc = check_ptr(dv, "dv", 16)) ||
+      (rc = check_ptr(dq_r, "dq_r", 16)) || (rc = check_ptr(dk_r, "dk_r", 16)))
+    return rc;
+  const Plan pl = make_plan(1, shape, R);
+  if (workspace_bytes < pl.total)
+    return fail(DF_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+  if ((rc = check_ptr(workspace, "workspace", kAlign))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  dfa::Params p = base_params(shape, span, buckets, att, R, pl, ws, key_mask, cu_seqlens);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qr = q_r;
+  p.kr = k_r;
+  p.out = const_cast<void*>(out);
+  p.lse = const_cast<float*>(lse);
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dqr = dq_r;
+  p.dkr = dk_r;
+  p.delta = reinterpret_cast<float*>(ws + pl.delta);
+  p.dq_acc = reinterpret_cast<float*>(ws + pl.dq_acc);
+  p.dk_acc = reinterpret_cast<float*>(ws + pl.dk_acc);
+  p.dc2p = ws + pl.dc2p;
+  p.dp2c = ws + pl.dp2c;
+  p.part = reinterpret_cast<float*>(ws + pl.part);
+  if (p.T > 0) {
+    if ((rc = hip_check(dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st), "relative index kernel")))
+      return rc;
+    if ((rc = hip_check(dfa::launch_strips(p, st), "strip kernel"))) return rc;
+    if ((rc = hip_check(dfa::launch_bwd_pre(p, st), "delta kernel"))) return rc;
+    if ((rc = hip_check(dfa::launch_bwd_dkv(p, st), "dk/dv kernel"))) return rc;
+    if ((rc = hip_check(dfa::launch_bwd_dq(p, st), "dq kernel"))) return rc;
+  }
+  // with no tokens this only writes zero dq_r / dk_r
+  if ((rc = hip_check(dfa::launch_relgrad(p, st), "relative gradient kernels"))) return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the kernels: dtype traits, MFMA
+// wrappers and the lane layout of a 32x32 MFMA accumulator on gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "params.hpp"
+
+namespace dfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// dtype traits. A 32x32 MFMA consumes, per lane, E consecutive elements of a
+// K-step of KS (16-bit types: 32x32x16, E = 8; fp32: 32x32x2, E = 1).
+//
+// Operand convention used everywhere: lane l feeds row (A) or column (B)
+// l % 32, from K-group g = l / 32; slot s of group g stands for contraction
+// index g*E + s of the step. The hardware pairs equal (group, slot) of A and
+// B, so any relabelling of the contraction index that both operands share
+// gives the same product.
+
+template <int DT> struct Tr;
+
+template <> struct Tr<DF_BF16_T> {
+  using T = uint16_t;
+  using frag = bf16x8;
+  static constexpr int E = 8, KS = 16;
+  static __device__ __forceinline__ float to_f(T x) { return __uint_as_float(uint32_t(x) << 16); }
+  static __device__ __forceinline__ T from_f(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag pack(const float* x) {
+    frag r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = (__bf16)x[s];
+    return r;
+  }
+  static __device__ __forceinline__ frag ld(const T* p) {  // 8 consecutive, 16-byte aligned
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ frag ld2x4(const T* p0, const T* p1) {  // 4 + 4 consecutive
+    uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
+    return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
+  }
+  static __device__ __forceinline__ frag zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+};
+
+template <> struct Tr<DF_FP16_T> {
+  using T = uint16_t;
+  using frag = f16x8;
+  static constexpr int E = 8, KS = 16;
+  static __device__ __forceinline__ float to_f(T x) { return (float)__builtin_bit_cast(_Float16, x); }
+  static __device__ __forceinline__ T from_f(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag pack(const float* x) {
+    frag r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = (_Float16)x[s];
+    return r;
+  }
+  static __device__ __forceinline__ frag ld(const T* p) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ frag ld2x4(const T* p0, const T* p1) {
+    uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
+    return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
+  }
+  static __device__ __forceinline__ frag zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+};
+
+template <> struct Tr<DF_FP32_T> {
+  using T = float;
+  using frag = float;
+  static constexpr int E = 1, KS = 2;
+  static __device__ __forceinline__ float to_f(T x) { return x; }
+  static __device__ __forceinline__ T from_f(float f) { return f; }
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag pack(const float* x) { return x[0]; }
+  static __device__ __forceinline__ frag ld(const T* p) { return *p; }
+  static __device__ __forceinline__ frag ld2x4(const T* p0, const T*) { return *p0; }
+  static __device__ __forceinline__ frag zero() { return 0.f; }
+};
+
+// ---------------------------------------------------------------------------
+// Accumulator layout of a 32x32 MFMA (C/D operand): lane l holds column
+// n = l % 32 and, in register v (0..15), row acc_row(v, l / 32).
+__device__ __forceinline__ constexpr int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
+
+// When a 32x32 accumulator tile is fed back as the B operand of a product
+// that contracts over its rows, step q of that product takes registers
+// v = q*E .. q*E + E - 1 from each lane. The other operand must then supply,
+// for lane group g and slot s, contraction index acc_row(q*E + s, g). For
+// 16-bit types these are two runs of four: [16q + 4g, +4) and [16q + 8 + 4g, +4).
+template <int E>
+__device__ __forceinline__ constexpr int fed_row(int q, int s, int g) { return acc_row(q * E + s, g); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Exchange with the lane 32 apart (lanes l and l ^ 32 hold the two halves of
+// an accumulator column).
+__device__ __forceinline__ float xor32(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(int(((threadIdx.x & 63) ^ 32) << 2), __float_as_int(x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sequence bounds of blockIdx.z: padded (cu == nullptr) or packed.
+struct SeqRange {
+  int64_t start;
+  int len;
+};
+__device__ __forceinline__ SeqRange seq_range(const int32_t* cu, int z, int Lmax) {
+  if (cu) {
+    int a = cu[z], b = cu[z + 1];
+    return {int64_t(a), b - a};
+  }
+  return {int64_t(z) * Lmax, Lmax};
+}
+
+}  // namespace dfa

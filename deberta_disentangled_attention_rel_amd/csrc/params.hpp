@@ -1,0 +1,56 @@
+// Internal parameter block and launcher declarations (host and device).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfa {
+
+constexpr int DF_BF16_T = 0, DF_FP16_T = 1, DF_FP32_T = 2;
+
+// Everything a kernel of the path may need. Pointers are device pointers.
+struct Params {
+  // shape
+  int nseq, Lmax, H, D, R, att, span, buckets, dtype;
+  int RP;                   // row pitch of every [H][T][.] strip: R rounded up to 8
+  int64_t T;
+  int64_t ts, hs;           // token / head element strides of [T,H,D] tensors
+  const int32_t* cu;        // [nseq+1] or nullptr (padded)
+  const uint8_t* kmask;     // [T] or nullptr
+  float scale;              // s = 1/sqrt(3D)
+  float scale_log2;         // s * log2(e)
+  // relative index tables, entry d + Lmax - 1
+  int32_t* c2p;
+  int32_t* p2c;
+  // user tensors
+  const void *q, *k, *v, *qr, *kr;
+  void* out;
+  float* lse;
+  const void* dout;
+  void *dq, *dk, *dv, *dqr, *dkr;
+  // workspace
+  void* c2ps;               // [H][T][RP] dtype: s*log2(e) * Q . K_r^T
+  void* p2cs;               // [H][T][RP] dtype: s*log2(e) * K . Q_r^T
+  void* ends;               // [4][H][T] dtype: c2ps[..][0], c2ps[..][R-1],
+                            //   p2cs[..][0], p2cs[..][R-1]
+  float* delta;             // [H][T]: rowsum(dO * O)
+  float* dq_acc;            // [H][T][D]: s * dS K
+  float* dk_acc;            // [H][T][D]: s * dS^T Q
+  void* dc2p;               // [H][T][RP] dtype: segmented sums of dS over delta(i,j)
+  void* dp2c;               // [H][T][RP] dtype: segmented sums of dS over delta(j,i)
+  float* part;              // [2][H][nchunk][R][D] split-K partials
+  int nchunk;
+  int chunk_tokens;
+};
+
+// launchers (each returns hipGetLastError() after its launches)
+hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st);
+hipError_t launch_strips(const Params& p, hipStream_t st);
+hipError_t launch_fwd(const Params& p, hipStream_t st);
+hipError_t launch_bwd_pre(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dkv(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq(const Params& p, hipStream_t st);
+hipError_t launch_relgrad(const Params& p, hipStream_t st);
+
+}  // namespace dfa

@@ -1,0 +1,208 @@
+// Relative-position gradients from the dense dC2P / dP2C strips
+// (DisentangledFlash 1.1.1 page, "Hugging Face usage": relative-position
+// projections stay in the autograd graph; "Performance": the 12LRD term of
+// the backward count).
+//
+//   dq   = dq_acc + s * dC2P K_r      dk   = dk_acc + s * dP2C Q_r      (per token)
+//   dk_r = s * sum_t dC2P[t]^T Q[t]    dq_r = s * sum_t dP2C[t]^T K[t]    (per head)
+//
+// The token sums are split into fixed chunks; each chunk's [R, D] partial is
+// written to the workspace and a second kernel adds the chunks in index
+// order. No atomics; the chunking depends only on the shape.
+#include "tiles.hpp"
+
+namespace dfa {
+
+namespace {
+
+// which = 0: dC2P with K_r into dq; which = 1: dP2C with Q_r into dk.
+// Workgroup: 128 tokens (4 waves x 32) x all D columns; loop over R in chunks
+// of RC rows, W^T chunk staged in LDS, strip rows read straight from global.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void dx_kernel(Params p) {
+  using TR = Tr<DT>;
+  using T = typename TR::T;
+  using frag = typename TR::frag;
+  constexpr int E = TR::E, KS = TR::KS, ND = D / 32;
+  constexpr int RC = 64;
+  constexpr int WTP = Pitch<T, RC>::rm;
+  __shared__ __align__(16) T Wt[D * WTP];
+
+  const int which = blockIdx.z;
+  const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int64_t t0 = int64_t(blockIdx.x) * 128 + wave * 32;
+  const int R = p.R, RP = p.RP;
+  const T* G = (const T*)(which ? p.dp2c : p.dc2p) + int64_t(h) * p.T * RP;
+  const T* W = (const T*)(which ? p.qr : p.kr) + int64_t(h) * R * D;
+  const float* acc_in = (which ? p.dk_acc : p.dq_acc) + int64_t(h) * p.T * D;
+  T* outp = (T*)(which ? p.dk : p.dq);
+
+  const int64_t ta = t0 + li;
+  const bool a_ok = ta < p.T;
+  const T* grow = G + (a_ok ? ta : 0) * RP;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
+
+  for (int r0 = 0; r0 < R; r0 += RC) {
+    __syncthreads();
+    stage_rows_tr<T, D, RC, WTP, WTP, 256>(nullptr, Wt, W, D, r0, R);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RC / KS; ++q) {
+      const int rr = r0 + q * KS + g * E;
+      frag a = (a_ok && rr < RP) ? TR::ld(grow + rr) : TR::zero();
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const T* wr = &Wt[(32 * nd + li) * WTP + q * KS + g * E];
+        frag b;
+        if constexpr (E == 8)
+          b = TR::ld2x4(wr, wr + 4);
+        else
+          b = TR::ld(wr);
+        acc[nd] = TR::mma(a, b, acc[nd]);
+      }
+    }
+  }
+  // C[m = token][n = d]: lane holds column d = 32nd + li, rows acc_row(v, g)
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t t = t0 + acc_row(v, g);
+      if (t >= p.T) continue;
+      const int c = 32 * nd + li;
+      const float val = acc_in[t * D + c] + p.scale * acc[nd][v];
+      outp[t * p.ts + int64_t(h) * p.hs + c] = TR::from_f(val);
+    }
+}
+
+// Split-K partials of dk_r (which = 0: dC2P^T Q) and dq_r (which = 1: dP2C^T K).
+// Workgroup: 128 strip rows r (4 waves x 32) x all D columns, over one chunk
+// of tokens, TK tokens at a time; both operands staged transposed in LDS.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void dw_kernel(Params p) {
+  using TR = Tr<DT>;
+  using T = typename TR::T;
+  using frag = typename TR::frag;
+  constexpr int E = TR::E, KS = TR::KS, ND = D / 32;
+  constexpr int RM = 128, TK = 32;
+  constexpr int GTP = Pitch<T, TK>::rm;
+  __shared__ __align__(16) T Gt[RM * GTP];
+  __shared__ __align__(16) T Xt[D * GTP];
+
+  const int which = blockIdx.z / p.H, h = blockIdx.z % p.H;
+  const int chunk = blockIdx.y;
+  const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * RM;
+  const int R = p.R, RP = p.RP;
+  const T* G = (const T*)(which ? p.dp2c : p.dc2p) + int64_t(h) * p.T * RP;
+  const T* X = (const T*)(which ? p.k : p.q) + int64_t(h) * p.hs;
+  const int64_t c0 = int64_t(chunk) * p.chunk_tokens;
+  const int64_t c1 = c0 + p.chunk_tokens < p.T ? c0 + p.chunk_tokens : p.T;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
+
+  for (int64_t tk = c0; tk < c1; tk += TK) {
+    const int nv = int(c1 - tk);  // valid tokens in this step (>= 1)
+    __syncthreads();
+    // Gt[r][t] from G rows t (RM columns starting at r0; columns >= RP -> 0)
+    {
+      constexpr int CH = 16 / sizeof(T);
+      for (int it = threadIdx.x; it < TK * (RM / CH); it += 256) {
+        const int t = it % TK, c = (it / TK) * CH;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (t < nv && r0 + c < RP) val = *reinterpret_cast<const uint4*>(G + (tk + t) * RP + r0 + c);
+        const T* ve = reinterpret_cast<const T*>(&val);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) Gt[(c + e) * GTP + t] = ve[e];
+      }
+    }
+    stage_rows_tr<T, D, TK, GTP, GTP, 256>(nullptr, Xt, X + tk * p.ts, p.ts, 0, nv);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TK / KS; ++q) {
+      const T* gr = &Gt[(32 * wave + li) * GTP + q * KS + g * E];
+      frag a;
+      if constexpr (E == 8)
+        a = TR::ld2x4(gr, gr + 4);
+      else
+        a = TR::ld(gr);
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const T* xr = &Xt[(32 * nd + li) * GTP + q * KS + g * E];
+        frag b;
+        if constexpr (E == 8)
+          b = TR::ld2x4(xr, xr + 4);
+        else
+          b = TR::ld(xr);
+        acc[nd] = TR::mma(a, b, acc[nd]);
+      }
+    }
+  }
+  float* part = p.part + ((int64_t(which) * p.H + h) * p.nchunk + chunk) * int64_t(R) * D;
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = r0 + 32 * wave + acc_row(v, g);
+      if (r < R) part[int64_t(r) * D + 32 * nd + li] = acc[nd][v];
+    }
+}
+
+// Fixed-order sum of the chunk partials: out[h][r][d] = s * sum_c part[c].
+template <int DT>
+__global__ __launch_bounds__(256) void reduce_kernel(Params p) {
+  using TR = Tr<DT>;
+  using T = typename TR::T;
+  const int64_t per = int64_t(p.R) * p.D;
+  const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = 2 * int64_t(p.H) * per;
+  if (n >= total) return;
+  const int64_t which = n / (int64_t(p.H) * per);
+  const int64_t rest = n % (int64_t(p.H) * per);
+  const int64_t h = rest / per, e = rest % per;
+  const float* part = p.part + (which * p.H + h) * p.nchunk * per + e;
+  float s = 0.f;
+  for (int c = 0; c < p.nchunk; ++c) s += part[c * per];
+  T* out = (T*)(which ? p.dqr : p.dkr);
+  out[h * per + e] = TR::from_f(s * p.scale);
+}
+
+template <int DT, int D>
+void launch_d(const Params& p, hipStream_t st) {
+  if (p.T > 0) {
+    dim3 g1(unsigned((p.T + 127) / 128), unsigned(p.H), 2u);
+    dx_kernel<DT, D><<<g1, 256, 0, st>>>(p);
+    dim3 g2(unsigned((p.R + 127) / 128), unsigned(p.nchunk), unsigned(2 * p.H));
+    dw_kernel<DT, D><<<g2, 256, 0, st>>>(p);
+  }
+  const int64_t total = 2 * int64_t(p.H) * p.R * p.D;
+  reduce_kernel<DT><<<unsigned((total + 255) / 256), 256, 0, st>>>(p);
+}
+
+template <int DT>
+void launch_dt(const Params& p, hipStream_t st) {
+  switch (p.D) {
+    case 32: launch_d<DT, 32>(p, st); break;
+    case 64: launch_d<DT, 64>(p, st); break;
+    default: launch_d<DT, 128>(p, st); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_relgrad(const Params& p, hipStream_t st) {
+  switch (p.dtype) {
+    case DF_BF16_T: launch_dt<DF_BF16_T>(p, st); break;
+    case DF_FP16_T: launch_dt<DF_FP16_T>(p, st); break;
+    default: launch_dt<DF_FP32_T>(p, st); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfa

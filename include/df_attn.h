@@ -1,0 +1,141 @@
+/*
+ * df_attn.h — exact disentangled (C2P/P2C) self-attention for AMD gfx950.
+ *
+ * The operation is the DeBERTa-v2/v3 attention that the DisentangledFlash
+ * 1.1.1 page describes ("Status": bidirectional DeBERTa-v2/v3-style C2P/P2C
+ * attention without the [B,H,L,L] matrix; FP16, BF16 and strict FP32; head
+ * dims 32, 64, 128; factorized 2-D padding masks; packed cu_seqlens layouts.
+ * "Hugging Face usage": an LSE-producing forward, and Q/K/V and
+ * relative-projection gradients). Per sequence and head, with local positions
+ * i (query) and j (key):
+ *
+ *   S[i,j] = s * ( Q_i.K_j + Q_i.K_r[delta(i,j)] + K_j.Q_r[delta(j,i)] ),
+ *   s = 1/sqrt(3*head_dim),
+ *   delta(a,b) = clamp(bucket(a-b) + att, 0, R-1),  R = 2*att,
+ *   att = buckets > 0 ? buckets : span,
+ *   bucket(d) = d                       if buckets == 0 or |d| <= buckets/2,
+ *             = sign(d)*(mid + ceil((mid-1)*ln(|d|/mid)/ln((span-1)/mid)))
+ *                                        otherwise (mid = buckets/2),
+ *   O_i = sum_j softmax_j(S[i,:]) V_j,   LSE_i = ln sum_j exp(S[i,j]).
+ *
+ * Pair (i,j) is scored only if both tokens are valid (factorized mask) and
+ * belong to the same sequence. A masked query row gets O = 0, LSE = -inf, and
+ * zero gradients.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and results are valid once that
+ *    stream has reached this point.
+ *  - Every argument is validated on the host before anything is enqueued. On
+ *    an error nothing is launched and the outputs are untouched; the code is
+ *    returned and df_last_error() describes the failed check. There is no
+ *    fallback path of any kind.
+ *  - q,k,v,out,dout,dq,dk,dv are [T, H, D] with element strides tok_stride
+ *    and head_stride (D contiguous; both strides multiples of 8 elements for
+ *    16-bit types and of 4 for fp32; base pointers 16-byte aligned).
+ *    q_r,k_r,dq_r,dk_r are contiguous [H, R, D]. lse is fp32 [H, T].
+ *  - key_mask: uint8 [T] (nonzero = valid token) or NULL (all valid).
+ *  - cu_seqlens: int32 [batch+1] on the device, or NULL for the padded layout
+ *    (batch sequences of max_seqlen tokens, T = batch*max_seqlen). With
+ *    cu_seqlens the caller guarantees cu_seqlens[0] = 0, non-decreasing,
+ *    cu_seqlens[batch] = T and every length <= max_seqlen (not checked: the
+ *    array lives on the device).
+ *  - The workspace is a caller-owned device buffer of at least
+ *    df_attn_workspace_size() bytes, 256-byte aligned. Its contents are
+ *    scratch and need no initialisation.
+ *  - Results are deterministic: the same inputs, shapes and device give
+ *    bitwise-identical outputs. No kernel uses atomics.
+ */
+#ifndef DF_ATTN_H
+#define DF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DF_BF16 = 0, DF_FP16 = 1, DF_FP32 = 2 } df_dtype;
+
+enum {
+  DF_OK = 0,
+  DF_ERR_INVALID = 1,      /* null pointer, bad shape/stride/alignment, R mismatch */
+  DF_ERR_UNSUPPORTED = 2,  /* head_dim not in {32,64,128}, unknown dtype */
+  DF_ERR_WORKSPACE = 3,    /* workspace smaller than df_attn_workspace_size() */
+  DF_ERR_HIP = 4           /* a HIP launch reported an error */
+};
+
+typedef struct {
+  int32_t batch;          /* number of sequences (padded: B) */
+  int32_t max_seqlen;     /* L (padded) or the longest sequence (packed) */
+  int64_t total_tokens;   /* T: batch*max_seqlen (padded) or cu_seqlens[batch] */
+  int32_t num_heads;      /* H */
+  int32_t head_dim;       /* D in {32, 64, 128} */
+  int32_t dtype;          /* df_dtype of q,k,v,q_r,k_r,out,dout and all gradients */
+  int64_t tok_stride;     /* element stride between tokens of [T,H,D] tensors */
+  int64_t head_stride;    /* element stride between heads of [T,H,D] tensors */
+} df_attn_shape;
+
+/* Non-raising eligibility check (the strict-contract idea of the
+ * FastFlashAttention page, "Strict policy + fallback"). Returns DF_OK when
+ * df_attn_fwd/df_attn_bwd accept this shape and index configuration, else the
+ * error code they would return. `span` is DeBERTa's max_relative_positions
+ * (>= 1), `buckets` its position_buckets (0 = no log bucketing; otherwise even,
+ * >= 2, with span-1 > buckets/2). Host only; touches no device. */
+int df_attn_supported(const df_attn_shape* shape, int32_t span, int32_t buckets);
+
+/* Bytes of workspace needed by df_attn_fwd (pass 0) or df_attn_bwd (pass 1);
+ * 0 if the arguments are invalid. Host only. */
+size_t df_attn_workspace_size(int pass, const df_attn_shape* shape,
+                              int32_t span, int32_t buckets);
+
+/* The relative-position index tables over d = i - j in
+ * [-(max_seqlen-1), max_seqlen-1], entry d + max_seqlen - 1:
+ *   c2p_lut[.] = delta(i, j)  (row of K_r used by query i against key j)
+ *   p2c_lut[.] = delta(j, i)  (row of Q_r used by key j against query i)
+ * Both are int32 device arrays of 2*max_seqlen-1 entries, written on `stream`.
+ * The ceiling of the log bucket is evaluated in fp64 with exact detection of
+ * integer arguments, so the tables are exact for every configuration whose
+ * ceiling arguments are not within ~1e-12 of an integer without being one. */
+int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets,
+                       int32_t* c2p_lut, int32_t* p2c_lut, void* stream);
+
+/* Forward pass: writes out [T,H,D] (dtype) and lse [H,T] (fp32, natural log;
+ * -inf on masked rows). q_r and k_r must have R = 2*att rows. */
+int df_attn_fwd(const df_attn_shape* shape,
+                const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r,
+                int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens,
+                void* out, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass: given the forward's out and lse and the output gradient
+ * dout, writes dq, dk, dv [T,H,D] and dq_r, dk_r [H,R,D] (all dtype). The
+ * gradients overwrite the outputs (never accumulate). Scores are recomputed
+ * from the inputs and lse; nothing of the forward's workspace is reused. */
+int df_attn_bwd(const df_attn_shape* shape,
+                const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r,
+                int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens,
+                const void* out, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of an error code. */
+const char* df_strerror(int code);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* df_last_error(void);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int df_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DF_ATTN_H */
