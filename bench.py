@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Forward+backward throughput of exact disentangled attention on one MI355X.
+
+Workload (the DisentangledFlash 1.1.1 page, "Performance": BF16, 12 heads,
+head dim 64, 16,384 active tokens, padded layout, all tokens active, no
+dropout): B=2, L=8192, H=12, D=64, log-bucketed relative index with
+position_buckets=256, max_relative_positions=512 (R=512), synthetic seeded
+inputs N(0, 1/D), dout N(0, 1).
+
+A step is one pass of the whole path: the forward (index tables, strips,
+fused forward) and the backward (index tables, strips, Delta, dK/dV, dQ,
+relative-gradient GEMMs). FLOPs per step follow the page's convention,
+B*H*(14 L^2 D + 16 L R D). Inputs, outputs and the workspace are resident in
+HBM before timing; nothing is allocated inside the timed region.
+
+Prints one JSON line. Per-kernel durations come from HIP events recorded by
+the library around each of its launches during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd TFLOP/s (BH(14L²D+16LRD)) L=8192 H=12 D=64 bf16; % MFMA peak"
+WORKLOAD = 3
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+# the pages' own latency for this exact workload (H200, DF Triton, fwd+bwd)
+PAGES_H200_FWD_BWD_MS = 53.80
+
+
+def flops_fwd_bwd(B, H, L, D, R):
+    return B * H * (14.0 * L * L * D + 16.0 * L * R * D)
+
+
+def kernel_algorithmic_flops(stage, B, H, L, D, R):
+    """Algorithmic FLOPs of one launch of a stage (matrix products it must run)."""
+    per = B * H * L * L * D
+    return {
+        "fwd": 4.0 * per,            # S = QK^T, O = PV
+        "bwd_dkv": 8.0 * per,        # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
+        "bwd_dq": 6.0 * per,         # S, dP, dQ = dS K
+        "strips": 2.0 * B * H * L * R * D,       # one of Q K_r^T / K Q_r^T
+        "relgrad_dx": 4.0 * B * H * L * R * D,   # dC2P K_r and dP2C Q_r
+        "relgrad_dw": 4.0 * B * H * L * R * D,   # dC2P^T Q and dP2C^T K
+    }.get(stage)
+
+
+def cpu_baseline(inp):
+    """The float64 oracle on one (sequence, head) slice of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle
+    w = inp.workload
+    L = inp.lengths[0]
+    f = inp.f64
+    sl = slice(0, L)
+    args = [f["q"][sl, :1], f["k"][sl, :1], f["v"][sl, :1], f["q_r"][:1], f["k_r"][:1]]
+    t0 = time.perf_counter()
+    oracle.forward(*args, w.span, w.buckets)
+    oracle.backward(*args, f["dout"][sl, :1], w.span, w.buckets)
+    dt = time.perf_counter() - t0
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    fl = flops_fwd_bwd(1, 1, L, w.head_dim, w.rows)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, forward then backward, one (sequence, head) slice "
+                      f"of the workload (L={L}, D={w.head_dim}, R={w.rows}); {dt:.1f} s wall; "
+                      f"scaled by the same FLOP convention"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        return 2
+
+    import torch
+    import deberta_disentangled_attention_rel_amd as df
+    from synth import workload_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    inp = workload_inputs(WORKLOAD)
+    w = inp.workload
+    B, L, H, D, R = inp.nseq, inp.max_seqlen, w.heads, w.head_dim, w.rows
+    t = {k: v.to(dev) for k, v in inp.t.items()}
+    q, k, v, dout = (t[n].view(B, L, H, D) for n in ("q", "k", "v", "dout"))
+    q_r, k_r = t["q_r"], t["k_r"]
+    shape = df.make_shape(q.view(B * L, H, D), B, L)
+    ws_bytes = max(df.workspace_size(0, shape, w.span, w.buckets),
+                   df.workspace_size(1, shape, w.span, w.buckets))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, B * L), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty_like(q_r), torch.empty_like(k_r))
+
+    # active relative rows (the page's R): distinct table entries reached at L
+    c2p, _ = df.build_rel_index(L, w.span, w.buckets, device=dev)
+    r_active = int(torch.unique(c2p).numel())
+
+    def step():
+        df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws)
+        df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    df.profile_enable(True)
+    df.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = df.profile_read()
+    df.profile_enable(False)
+
+    ms = (t1 - t0) * 1e3 / a.steps
+    fl = flops_fwd_bwd(B, H, L, D, r_active)
+    tflops = fl / (ms * 1e-3) / 1e12
+    kern = {n: {"ms_per_launch": round(tot / cnt, 4), "launches_per_step": cnt / a.steps}
+            for n, (tot, cnt) in stages.items() if cnt > 0}
+    dom = max((n for n in kern if kernel_algorithmic_flops(n, B, H, L, D, R) is not None),
+              key=lambda n: stages[n][0])
+    dom_ms = stages[dom][0] / stages[dom][1]
+    dom_tf = kernel_algorithmic_flops(dom, B, H, L, D, R) / (dom_ms * 1e-3) / 1e12
+    bound = "mfma"
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(PAGES_H200_FWD_BWD_MS / ms, 3),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": L, "heads": H, "head_dim": D,
+                   "tokens": B * L, "layout": "padded", "position_buckets": w.buckets,
+                   "max_relative_positions": w.span, "rel_rows": R, "rel_rows_active": r_active},
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels": kern,
+        "device": torch.cuda.get_device_properties(dev).name,
+        "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

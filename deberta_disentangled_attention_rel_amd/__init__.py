@@ -18,13 +18,15 @@ from typing import Optional
 import torch
 
 __all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "bwd",
-           "DfError", "DTYPE_CODES", "LIB_PATH"]
+           "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
 DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
-            "df_attn_fwd", "df_attn_bwd", "df_strerror", "df_last_error", "df_attn_version")
+            "df_attn_fwd", "df_attn_bwd", "df_strerror", "df_last_error", "df_attn_version",
+            "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name")
+NUM_STAGES = 9
 
 
 class DfError(RuntimeError):
@@ -73,6 +75,13 @@ def lib() -> ctypes.CDLL:
     L.df_last_error.restype = ctypes.c_char_p
     L.df_attn_version.argtypes = []
     L.df_attn_version.restype = ctypes.c_int
+    L.df_attn_profile_enable.argtypes = [ctypes.c_int]
+    L.df_attn_profile_enable.restype = ctypes.c_int
+    L.df_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.c_int]
+    L.df_attn_profile_read.restype = ctypes.c_int
+    L.df_attn_stage_name.argtypes = [ctypes.c_int]
+    L.df_attn_stage_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -124,6 +133,20 @@ def _layout(q, k, v, cu_seqlens, max_seqlen):
         batch = q.shape[0] // L
     q3, k3, v3 = (_as_thd(x).contiguous() for x in (q, k, v))
     return q3, k3, v3, batch, L
+
+
+def profile_enable(on: bool) -> None:
+    """Turn per-launch HIP event timing inside the library on or off."""
+    _check(lib().df_attn_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """``{stage_name: (total_ms, launches)}`` since the last read (waits for the events)."""
+    ms = (ctypes.c_float * NUM_STAGES)()
+    n = (ctypes.c_int * NUM_STAGES)()
+    _check(lib().df_attn_profile_read(ms, n, NUM_STAGES))
+    L = lib()
+    return {L.df_attn_stage_name(i).decode(): (float(ms[i]), int(n[i])) for i in range(NUM_STAGES)}
 
 
 def build_rel_index(max_seqlen: int, span: int, buckets: int, device="cuda"):

@@ -183,6 +183,33 @@ int hip_check(hipError_t e, const char* what) {
   return DF_OK;
 }
 
+// Optional per-launch event timing (df_attn_profile_*).
+struct Profiler {
+  static constexpr int kCap = 4096;
+  bool on = false;
+  int n = 0;
+  int stage[kCap];
+  hipEvent_t ev[2 * kCap];
+};
+Profiler g_prof;
+
+const char* const kStageNames[DF_NUM_STAGES] = {
+    "rel_index", "strips", "fwd", "delta", "bwd_dkv", "bwd_dq", "relgrad_dx", "relgrad_dw", "relgrad_sum"};
+
+// Run one launcher as stage `stage`, bracketed by events when profiling.
+template <class F>
+int run_stage(int stage, hipStream_t st, const char* what, F&& launch) {
+  const bool rec = g_prof.on && g_prof.n < Profiler::kCap;
+  const int k = rec ? g_prof.n++ : 0;
+  if (rec) {
+    g_prof.stage[k] = stage;
+    hipEventRecord(g_prof.ev[2 * k], st);
+  }
+  const hipError_t e = launch();
+  if (rec) hipEventRecord(g_prof.ev[2 * k + 1], st);
+  return hip_check(e, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +228,48 @@ const char* df_strerror(int code) {
 }
 
 const char* df_last_error(void) { return g_last_error.c_str(); }
+
+int df_attn_profile_enable(int on) {
+  if (on && !g_prof.on) {
+    for (int k = 0; k < 2 * Profiler::kCap; ++k) {
+      const hipError_t e = hipEventCreate(&g_prof.ev[k]);
+      if (e != hipSuccess) {
+        for (int j = 0; j < k; ++j) hipEventDestroy(g_prof.ev[j]);
+        return hip_check(e, "hipEventCreate");
+      }
+    }
+    g_prof.on = true;
+    g_prof.n = 0;
+  } else if (!on && g_prof.on) {
+    for (int k = 0; k < 2 * Profiler::kCap; ++k) hipEventDestroy(g_prof.ev[k]);
+    g_prof.on = false;
+    g_prof.n = 0;
+  }
+  return ok();
+}
+
+int df_attn_profile_read(float* ms, int* launches, int n_stages) {
+  if (!ms || !launches || n_stages < 0) return fail(DF_ERR_INVALID, "profile arrays must not be NULL");
+  if (!g_prof.on) return fail(DF_ERR_INVALID, "profiling is not enabled");
+  for (int k = 0; k < g_prof.n; ++k) {
+    int rc = hip_check(hipEventSynchronize(g_prof.ev[2 * k + 1]), "hipEventSynchronize");
+    if (rc) return rc;
+    float t = 0.f;
+    rc = hip_check(hipEventElapsedTime(&t, g_prof.ev[2 * k], g_prof.ev[2 * k + 1]), "hipEventElapsedTime");
+    if (rc) return rc;
+    const int sidx = g_prof.stage[k];
+    if (sidx < n_stages) {
+      ms[sidx] += t;
+      launches[sidx] += 1;
+    }
+  }
+  g_prof.n = 0;
+  return ok();
+}
+
+const char* df_attn_stage_name(int stage) {
+  return (stage >= 0 && stage < DF_NUM_STAGES) ? kStageNames[stage] : "";
+}
 
 int df_attn_supported(const df_attn_shape* shape, int32_t span, int32_t buckets) {
   int att, R;
@@ -253,10 +322,12 @@ int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const 
   p.out = out;
   p.lse = lse;
   if (p.T == 0) return ok();
-  if ((rc = hip_check(dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st), "relative index kernel")))
+  if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
+                     [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+      (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
+      (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
+      (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
     return rc;
-  if ((rc = hip_check(dfa::launch_strips(p, st), "strip kernel"))) return rc;
-  if ((rc = hip_check(dfa::launch_fwd(p, st), "forward kernel"))) return rc;
   return ok();
 }
 
@@ -302,15 +373,23 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
   p.dp2c = ws + pl.dp2c;
   p.part = reinterpret_cast<float*>(ws + pl.part);
   if (p.T > 0) {
-    if ((rc = hip_check(dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st), "relative index kernel")))
+    if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
+                       [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
+        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
+        (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
+        (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||
+        (rc = run_stage(DF_STAGE_DQ, st, "dq kernel", [&] { return dfa::launch_bwd_dq(p, st); })) ||
+        (rc = run_stage(DF_STAGE_RELGRAD_DX, st, "relative gradient kernel",
+                        [&] { return dfa::launch_relgrad_dx(p, st); })) ||
+        (rc = run_stage(DF_STAGE_RELGRAD_DW, st, "relative gradient kernel",
+                        [&] { return dfa::launch_relgrad_dw(p, st); })))
       return rc;
-    if ((rc = hip_check(dfa::launch_strips(p, st), "strip kernel"))) return rc;
-    if ((rc = hip_check(dfa::launch_bwd_pre(p, st), "delta kernel"))) return rc;
-    if ((rc = hip_check(dfa::launch_bwd_dkv(p, st), "dk/dv kernel"))) return rc;
-    if ((rc = hip_check(dfa::launch_bwd_dq(p, st), "dq kernel"))) return rc;
   }
   // with no tokens this only writes zero dq_r / dk_r
-  if ((rc = hip_check(dfa::launch_relgrad(p, st), "relative gradient kernels"))) return rc;
+  if ((rc = run_stage(DF_STAGE_RELGRAD_SUM, st, "relative gradient sum kernel",
+                     [&] { return dfa::launch_relgrad_sum(p, st); })))
+    return rc;
   return ok();
 }
 

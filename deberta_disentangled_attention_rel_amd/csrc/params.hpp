@@ -46,11 +46,13 @@ struct Params {
 
 // launchers (each returns hipGetLastError() after its launches)
 hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st);
-hipError_t launch_strips(const Params& p, hipStream_t st);
+hipError_t launch_strips(const Params& p, int which, hipStream_t st);  // 0: C2P, 1: P2C
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkv(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq(const Params& p, hipStream_t st);
-hipError_t launch_relgrad(const Params& p, hipStream_t st);
+hipError_t launch_relgrad_dx(const Params& p, hipStream_t st);
+hipError_t launch_relgrad_dw(const Params& p, hipStream_t st);
+hipError_t launch_relgrad_sum(const Params& p, hipStream_t st);
 
 }  // namespace dfa

@@ -174,33 +174,61 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
 }
 
 template <int DT, int D>
-void launch_d(const Params& p, hipStream_t st) {
-  if (p.T > 0) {
-    dim3 g1(unsigned((p.T + 127) / 128), unsigned(p.H), 2u);
-    dx_kernel<DT, D><<<g1, 256, 0, st>>>(p);
-    dim3 g2(unsigned((p.R + 127) / 128), unsigned(p.nchunk), unsigned(2 * p.H));
-    dw_kernel<DT, D><<<g2, 256, 0, st>>>(p);
-  }
+void launch_dx_d(const Params& p, hipStream_t st) {
+  dim3 g1(unsigned((p.T + 127) / 128), unsigned(p.H), 2u);
+  dx_kernel<DT, D><<<g1, 256, 0, st>>>(p);
+}
+
+template <int DT, int D>
+void launch_dw_d(const Params& p, hipStream_t st) {
+  dim3 g2(unsigned((p.R + 127) / 128), unsigned(p.nchunk), unsigned(2 * p.H));
+  dw_kernel<DT, D><<<g2, 256, 0, st>>>(p);
+}
+
+template <int DT>
+void launch_sum_dt(const Params& p, hipStream_t st) {
   const int64_t total = 2 * int64_t(p.H) * p.R * p.D;
   reduce_kernel<DT><<<unsigned((total + 255) / 256), 256, 0, st>>>(p);
 }
 
-template <int DT>
-void launch_dt(const Params& p, hipStream_t st) {
-  switch (p.D) {
-    case 32: launch_d<DT, 32>(p, st); break;
-    case 64: launch_d<DT, 64>(p, st); break;
-    default: launch_d<DT, 128>(p, st); break;
+#define DF_DISPATCH(FN, p, st)                                   \
+  switch (p.dtype) {                                             \
+    case DF_BF16_T:                                              \
+      if (p.D == 32) FN<DF_BF16_T, 32>(p, st);                   \
+      else if (p.D == 64) FN<DF_BF16_T, 64>(p, st);              \
+      else FN<DF_BF16_T, 128>(p, st);                            \
+      break;                                                     \
+    case DF_FP16_T:                                              \
+      if (p.D == 32) FN<DF_FP16_T, 32>(p, st);                   \
+      else if (p.D == 64) FN<DF_FP16_T, 64>(p, st);              \
+      else FN<DF_FP16_T, 128>(p, st);                            \
+      break;                                                     \
+    default:                                                     \
+      if (p.D == 32) FN<DF_FP32_T, 32>(p, st);                   \
+      else if (p.D == 64) FN<DF_FP32_T, 64>(p, st);              \
+      else FN<DF_FP32_T, 128>(p, st);                            \
+      break;                                                     \
   }
-}
 
 }  // namespace
 
-hipError_t launch_relgrad(const Params& p, hipStream_t st) {
+hipError_t launch_relgrad_dx(const Params& p, hipStream_t st) {
+  if (p.T == 0) return hipSuccess;
+  DF_DISPATCH(launch_dx_d, p, st)
+  return hipGetLastError();
+}
+
+hipError_t launch_relgrad_dw(const Params& p, hipStream_t st) {
+  if (p.T == 0) return hipSuccess;
+  DF_DISPATCH(launch_dw_d, p, st)
+  return hipGetLastError();
+}
+
+hipError_t launch_relgrad_sum(const Params& p, hipStream_t st) {
   switch (p.dtype) {
-    case DF_BF16_T: launch_dt<DF_BF16_T>(p, st); break;
-    case DF_FP16_T: launch_dt<DF_FP16_T>(p, st); break;
-    default: launch_dt<DF_FP32_T>(p, st); break;
+    case DF_BF16_T: launch_sum_dt<DF_BF16_T>(p, st); break;
+    case DF_FP16_T: launch_sum_dt<DF_FP16_T>(p, st); break;
+    default: launch_sum_dt<DF_FP32_T>(p, st); break;
   }
   return hipGetLastError();
 }

@@ -73,27 +73,25 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p, int which) {
 }
 
 template <int DT>
-hipError_t launch_strips_dt(const Params& p, hipStream_t st) {
+void launch_strips_dt(const Params& p, int which, hipStream_t st) {
   dim3 grid(unsigned((p.T + 127) / 128), unsigned((p.R + 63) / 64), unsigned(p.H));
-  for (int which = 0; which < 2; ++which) {
-    switch (p.D) {
-      case 32: strip_kernel<DT, 32><<<grid, 256, 0, st>>>(p, which); break;
-      case 64: strip_kernel<DT, 64><<<grid, 256, 0, st>>>(p, which); break;
-      default: strip_kernel<DT, 128><<<grid, 256, 0, st>>>(p, which); break;
-    }
+  switch (p.D) {
+    case 32: strip_kernel<DT, 32><<<grid, 256, 0, st>>>(p, which); break;
+    case 64: strip_kernel<DT, 64><<<grid, 256, 0, st>>>(p, which); break;
+    default: strip_kernel<DT, 128><<<grid, 256, 0, st>>>(p, which); break;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_strips(const Params& p, hipStream_t st) {
+hipError_t launch_strips(const Params& p, int which, hipStream_t st) {
   if (p.T == 0) return hipSuccess;
   switch (p.dtype) {
-    case DF_BF16_T: return launch_strips_dt<DF_BF16_T>(p, st);
-    case DF_FP16_T: return launch_strips_dt<DF_FP16_T>(p, st);
-    default: return launch_strips_dt<DF_FP32_T>(p, st);
+    case DF_BF16_T: launch_strips_dt<DF_BF16_T>(p, which, st); break;
+    case DF_FP16_T: launch_strips_dt<DF_FP16_T>(p, which, st); break;
+    default: launch_strips_dt<DF_FP32_T>(p, which, st); break;
   }
+  return hipGetLastError();
 }
 
 }  // namespace dfa

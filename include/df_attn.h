@@ -82,7 +82,7 @@ typedef struct {
  * FastFlashAttention page, "Strict policy + fallback"). Returns DF_OK when
  * df_attn_fwd/df_attn_bwd accept this shape and index configuration, else the
  * error code they would return. `span` is DeBERTa's max_relative_positions
- * (>= 1), `buckets` its position_buckets (0 = no log bucketing; otherwise even,
+ * (>= 1), `buckets` its position_buckets (0 = no log bucketing; otherwise
  * >= 2, with span-1 > buckets/2). Host only; touches no device. */
 int df_attn_supported(const df_attn_shape* shape, int32_t span, int32_t buckets);
 
@@ -130,6 +130,24 @@ const char* df_strerror(int code);
 
 /* Description of the last error returned on the calling thread ("" if none). */
 const char* df_last_error(void);
+
+/* Per-kernel timing for measurement. df_attn_profile_enable(1) creates a pool
+ * of HIP events (no device memory); while enabled, every kernel launch of
+ * df_attn_fwd / df_attn_bwd is bracketed by two events recorded on the
+ * caller's stream. df_attn_profile_read() waits for the recorded events, adds
+ * the elapsed milliseconds of each launch to ms[stage] and the launch count to
+ * launches[stage] for stage < n_stages (arrays of at least n_stages entries,
+ * zeroed by the caller), and forgets the records. Launches beyond the pool
+ * (4096 per read) are not timed. df_attn_profile_enable(0) releases the pool.
+ * Not thread-safe; meant for a single benchmarking thread. */
+enum {
+  DF_STAGE_INDEX = 0, DF_STAGE_STRIPS = 1, DF_STAGE_FWD = 2, DF_STAGE_DELTA = 3,
+  DF_STAGE_DKV = 4, DF_STAGE_DQ = 5, DF_STAGE_RELGRAD_DX = 6, DF_STAGE_RELGRAD_DW = 7,
+  DF_STAGE_RELGRAD_SUM = 8, DF_NUM_STAGES = 9
+};
+int df_attn_profile_enable(int on);
+int df_attn_profile_read(float* ms, int* launches, int n_stages);
+const char* df_attn_stage_name(int stage);
 
 /* Library version, as major*10000 + minor*100 + patch. */
 int df_attn_version(void);
