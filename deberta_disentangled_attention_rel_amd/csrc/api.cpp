@@ -110,7 +110,7 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
     o = align_up(o + bytes, kAlign);
     return at;
   };
-  pl.lut = take(2 * (2 * size_t(s->max_seqlen) - 1) * sizeof(int32_t));
+  pl.lut = take((2 * (2 * size_t(s->max_seqlen) - 1) + 2) * sizeof(int32_t));
   pl.c2ps = take(H * T * pl.RP * es);
   pl.p2cs = take(H * T * pl.RP * es);
   pl.ends = take(4 * H * T * es);
@@ -138,6 +138,19 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
   }
   pl.total = o;
   return pl;
+}
+
+// Whether consecutive d never move either table by more than one row. The
+// log part x(a) = (mid-1) ln(a/mid) / ln((span-1)/mid) has its largest slope,
+// (mid-1) / (mid ln((span-1)/mid)), at a = mid; when that is at most one, the
+// ceiling never skips a value (and the step from the identity part at mid is
+// one). A small margin keeps borderline cases on the general path.
+bool narrow_tables(int span, int buckets) {
+  if (buckets <= 0) return true;
+  const int mid = buckets / 2;
+  if (mid <= 1) return true;
+  const double slope = double(mid - 1) / (double(mid) * std::log(double(span - 1) / double(mid)));
+  return slope <= 1.0 - 1e-9;
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -170,6 +183,8 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
   p.scale_log2 = float(1.4426950408889634 / std::sqrt(3.0 * s->head_dim));
   p.c2p = reinterpret_cast<int32_t*>(ws + pl.lut);
   p.p2c = p.c2p + (2 * size_t(s->max_seqlen) - 1);
+  p.fbounds = p.p2c + (2 * size_t(s->max_seqlen) - 1);
+  p.narrow = narrow_tables(span, buckets) ? 1 : 0;
   p.c2ps = ws + pl.c2ps;
   p.p2cs = ws + pl.p2cs;
   p.ends = ws + pl.ends;
@@ -324,6 +339,8 @@ int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                      [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+      (rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
+                      [&] { return dfa::launch_lut_bounds(p.Lmax, p.R, p.c2p, p.p2c, p.fbounds, st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
@@ -375,6 +392,8 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                        [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+        (rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
+                        [&] { return dfa::launch_lut_bounds(p.Lmax, p.R, p.c2p, p.p2c, p.fbounds, st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||

@@ -1,0 +1,78 @@
+// Tile classes and LDS staging of the relative-position terms.
+//
+// A tile covers queries [i0, i0+BM) and keys [j0, j0+BN); its pairs have
+// d = i - j in [dlo, dhi] = [i0 - j0 - BN + 1, i0 + BM - 1 - j0].
+//  * far-left  (dlo >= d_hi): every pair uses C2P row R-1 and P2C row 0, so
+//    the C2P term is one value per query and the P2C term one value per key;
+//  * far-right (dhi <= d_lo): C2P row 0 and P2C row R-1, likewise;
+//  * band: anything else. The pair's rows come from the index tables (a
+//    slice of BM+BN-1 entries, packed c2p | p2c << 16, staged in LDS) and
+//    the values from LDS windows of the strips:
+//      C2P window, one row per query il: strip columns [cs_il, cs_il + BN + 8)
+//        with cs_il = c2p[i0+il - (j0+BN-1)] rounded down to 8 (the smallest
+//        row the query meets in this tile);
+//      P2C window, one row per key jl: columns [ps_jl, ps_jl + BM + 8) with
+//        ps_jl = p2c[i0+BM-1 - (j0+jl)] rounded down to 8.
+//    When no table ever steps by more than one row ("narrow" tables), BN
+//    consecutive d meet at most BN rows, so the windows hold every value the
+//    tile needs.
+#pragma once
+
+#include "tiles.hpp"
+
+namespace dfa {
+
+enum { TILE_BAND = 0, TILE_FAR_LEFT = 1, TILE_FAR_RIGHT = 2 };
+
+__device__ __forceinline__ int tile_class(int dlo, int dhi, int d_hi, int d_lo) {
+  if (dlo >= d_hi) return TILE_FAR_LEFT;
+  if (dhi <= d_lo) return TILE_FAR_RIGHT;
+  return TILE_BAND;
+}
+
+// ends[4][H][T]: C2P column 0, C2P column R-1, P2C column 0, P2C column R-1.
+// Index of the end array holding a tile's per-query C2P / per-key P2C value.
+__device__ __forceinline__ int c2p_end_of(int cls) { return cls == TILE_FAR_LEFT ? 1 : 0; }
+__device__ __forceinline__ int p2c_end_of(int cls) { return cls == TILE_FAR_LEFT ? 2 : 3; }
+
+// Packed table entry for d (clamped to the table).
+__device__ __forceinline__ uint32_t lut_entry(const Params& p, int d) {
+  const int off = p.Lmax - 1;
+  const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
+  return uint32_t(p.c2p[n]) | (uint32_t(p.p2c[n]) << 16);
+}
+
+__device__ __forceinline__ int lut_c(uint32_t e) { return int(e & 0xffffu); }
+__device__ __forceinline__ int lut_p(uint32_t e) { return int(e >> 16); }
+
+// Row pitches (elements) of the strip windows: an odd number of dwords for
+// 16-bit types (odd number of floats for fp32), so that lanes reading
+// different rows at nearby columns fall in different banks.
+template <typename T, int W> struct WinPitch {
+  static constexpr int v = sizeof(T) == 2 ? W + 2 : W + 1;
+};
+
+// Stage `rows` skewed strip rows into LDS. Row r reads strip row
+// base_row + min(row0 + r, nvalid - 1) (clamped so every load is in bounds),
+// columns [start(r), start(r) + WCOLS) where start(r) is a multiple of 8;
+// columns at or past RP are zero.
+template <typename T, int WCOLS, int PITCH, int NT, class StartFn>
+__device__ __forceinline__ void stage_window(T* __restrict__ dst, const T* __restrict__ strip, int RP,
+                                             int rows, int row0, int nvalid, StartFn start) {
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int NC = WCOLS / CH;
+  for (int it = threadIdx.x; it < rows * NC; it += NT) {
+    const int r = it / NC, c = (it % NC) * CH;
+    const int col = start(r) + c;
+    const int rr = min(row0 + r, nvalid - 1);
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (col < RP) val = *reinterpret_cast<const uint4*>(strip + int64_t(rr) * RP + col);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + r * PITCH + c);
+    d[0] = val.x;
+    d[1] = val.y;
+    d[2] = val.z;
+    d[3] = val.w;
+  }
+}
+
+}  // namespace dfa

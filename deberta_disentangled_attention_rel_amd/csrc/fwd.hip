@@ -3,50 +3,66 @@
 // usage": the LSE-producing training forward).
 //
 // Work item: one sequence, one head, 128 query rows (4 waves x 32). The key
-// loop walks 32*NKT keys at a time; K and V^T tiles are staged in LDS.
+// loop walks BN = 32*NKT keys at a time. The next key tile (K rows, V rows
+// transposed, per-key P2C far-field values with the key mask folded in, and
+// the index-table slice) is loaded into registers while the current one is
+// computed, then written to the other half of a double-buffered LDS area:
+// one barrier per tile.
 //
-// Layout: each wave computes S^T = K Q^T with 32x32 MFMAs, so lane l owns
-// query row l % 32 and holds 16 of every 32 keys; the other 16 sit in lane
-// l ^ 32. Row max and row sum are lane-local plus one exchange. The output is
-// accumulated transposed, O^T = V^T P^T, so the per-row rescale is lane-local
-// too and P feeds the MFMA straight from the score registers.
+// Each wave computes S^T = K Q^T with 32x32 MFMAs, so lane l owns query row
+// l % 32 and holds 16 of every 32 keys (the other 16 sit in lane l ^ 32).
+// Row max and row sum are lane-local plus one exchange; the output is
+// accumulated transposed, O^T = V^T P^T, so the rescale is lane-local and P
+// feeds the MFMA straight from the score registers.
 //
-// Scores are formed in the log2 domain: x = s*log2(e)*QK + C2P + P2C with the
-// strips pre-scaled. A tile whose pairs all sit in the saturated far field
-// (both index tables constant and at an end row) adds a per-row C2P value and
-// a per-key P2C value; any other tile gathers both terms per pair through the
-// index tables staged in LDS.
-#include "tiles.hpp"
+// Scores are in the log2 domain: y = s*log2(e)*QK + (relative terms). In a
+// far-field tile the per-key P2C value is added in the same FMA and the
+// per-query C2P value a is folded into the row max (exp2(y - (m - a))). A
+// band tile stages the strip windows it needs in LDS and gathers both terms
+// per pair from there (or from global memory when the tables can skip rows).
+#include "band.hpp"
 
 namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NKT>
-__global__ __launch_bounds__(256) void fwd_kernel(Params p) {
+template <int DT, int D, int NKT, bool NARROW>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
-  constexpr int BM = 128, BN = 32 * NKT;
+  constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
   constexpr int KP = Pitch<T, D>::rm, VP = Pitch<T, BN>::tr;
-  constexpr int NL = BM + BN - 1;
+  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
+  constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
+  static_assert(NL <= 256, "one table entry per thread");
+  // prefetch shapes: K rows as 16-byte chunks; V rows as (16-bit) row pairs
+  constexpr int KCH = BN * (D / CH), KPT = (KCH + 255) / 256;
+  constexpr bool PAIR = sizeof(T) == 2;
+  constexpr int VIT = PAIR ? (BN / 2) * (D / CH) : BN * (D / CH), VPT = (VIT + 255) / 256;
 
-  __shared__ __align__(16) T Ks[BN * KP];
-  __shared__ __align__(16) T Vt[D * VP];
-  __shared__ int lutc[NL], lutp[NL];
-  __shared__ __align__(16) float bj_s[BN];
-  __shared__ __align__(16) float kb_s[BN];
+  __shared__ __align__(16) T Ks[2][BN * KP];
+  __shared__ __align__(16) T Vt[2][D * VP];
+  __shared__ __align__(16) float bj_s[2][BN];
+  __shared__ uint32_t lut_s[2][NL];
+  __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
+  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
+  __shared__ int ps_s[NARROW ? BN : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
   const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * BM;
   if (i0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
-  const int R = p.R, RP = p.RP, off = p.Lmax - 1;
+  const int RP = p.RP;
+  const int d_hi = p.fbounds[0], d_lo = p.fbounds[1];
 
-  const int iw = i0 + wave * 32 + li;  // this lane's query (local index)
+  const int il = wave * 32 + li;
+  const int iw = i0 + il;  // this lane's query (local index)
   const bool qin = iw < sq.len;
   const int64_t tok_i = sq.start + (qin ? iw : sq.len - 1);
   const bool qvalid = qin && (!p.kmask || p.kmask[tok_i]);
@@ -57,13 +73,94 @@ __global__ __launch_bounds__(256) void fwd_kernel(Params p) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) Qf[q] = TR::ld(qp + q * KS + g * E);
   }
-  const T* ends = (const T*)p.ends;
-  const float a_end0 = TR::to_f(ends[int64_t(h) * T_ + tok_i]);
-  const float a_end1 = TR::to_f(ends[HT + int64_t(h) * T_ + tok_i]);
-  const T* c2prow = (const T*)p.c2ps + (int64_t(h) * T_ + tok_i) * RP;
-  const T* p2cbase = (const T*)p.p2cs + (int64_t(h) * T_ + sq.start) * RP;
+  const T* ends = (const T*)p.ends + int64_t(h) * T_;
+  const float a_end0 = TR::to_f(ends[tok_i]);
+  const float a_end1 = TR::to_f(ends[HT + tok_i]);
+  const T* c2pstrip = (const T*)p.c2ps + (int64_t(h) * T_ + sq.start) * RP;
+  const T* p2cstrip = (const T*)p.p2cs + (int64_t(h) * T_ + sq.start) * RP;
   const T* kbase = (const T*)p.k + sq.start * p.ts + int64_t(h) * p.hs;
   const T* vbase = (const T*)p.v + sq.start * p.ts + int64_t(h) * p.hs;
+  const uint8_t* kmask = p.kmask ? p.kmask + sq.start : nullptr;
+
+  auto cls_of = [&](int kb) {
+    const int j0 = kb * BN;
+    return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
+  };
+
+  // ---- next-tile registers
+  uint4 kreg[KPT];
+  uint4 vreg[VPT][PAIR ? 2 : 1];
+  float breg = 0.f;
+  uint32_t lreg = 0;
+
+  auto prefetch = [&](int kb) {
+    const int j0 = kb * BN;
+    const int cls = cls_of(kb);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = tid + u * 256;
+      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
+      kreg[u] = make_uint4(0, 0, 0, 0);
+      if (it < KCH && j0 + r < sq.len) kreg[u] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = tid + u * 256;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
+        vreg[u][0] = vreg[u][1] = make_uint4(0, 0, 0, 0);
+        if (it < VIT && j0 + r < sq.len) vreg[u][0] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
+        if (it < VIT && j0 + r + 1 < sq.len)
+          vreg[u][1] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r + 1) * p.ts + c);
+      } else {
+        const int r = it % BN, c = (it / BN) * CH;
+        vreg[u][0] = make_uint4(0, 0, 0, 0);
+        if (it < VIT && j0 + r < sq.len) vreg[u][0] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
+      }
+    }
+    if (tid < BN) {
+      const int j = j0 + tid;
+      const bool in = j < sq.len;
+      const int jc = in ? j : sq.len - 1;
+      const bool ok = in && (!kmask || kmask[jc]);
+      float b = 0.f;
+      if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
+      breg = ok ? b : -INFINITY;
+    }
+    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+  };
+
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = tid + u * 256;
+      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
+      if (it < KCH) *reinterpret_cast<uint4*>(&Ks[buf][r * KP + c]) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = tid + u * 256;
+      if (it >= VIT) continue;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
+        const uint32_t aw[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
+        const uint32_t bw[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          *reinterpret_cast<uint32_t*>(&Vt[buf][(c + e) * VP + r]) = lo | (hi << 16);
+        }
+      } else {
+        const int r = it % BN, c = (it / BN) * CH;
+        const float* f = reinterpret_cast<const float*>(&vreg[u][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(Vt[buf])[(c + e) * VP + r] = f[e];
+      }
+    }
+    if (tid < BN) bj_s[buf][tid] = breg;
+    if (tid < NL) lut_s[buf][tid] = lreg;
+  };
 
   f32x16 O[ND];
 #pragma unroll
@@ -71,92 +168,94 @@ __global__ __launch_bounds__(256) void fwd_kernel(Params p) {
   float m = -INFINITY, l = 0.f;
 
   const int nkb = (sq.len + BN - 1) / BN;
+  prefetch(0);
+  commit(0);
+  __syncthreads();
+
   for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
     const int j0 = kb * BN;
-    __syncthreads();
-    stage_rows<T, D, BN, KP, 256>(Ks, kbase, p.ts, j0, sq.len);
-    stage_rows_tr<T, D, BN, KP, VP, 256>(nullptr, Vt, vbase, p.ts, j0, sq.len);
+    const int cls = cls_of(kb);
+    if (kb + 1 < nkb) prefetch(kb + 1);
 
-    // tile class (uniform): are both tables constant at an end row?
-    const int dlo = i0 - (j0 + BN - 1), dhi = i0 + BM - 1 - j0;
-    auto cl = [&](int d) { return d < -off ? 0 : (d > off ? 2 * off : d + off); };
-    const int clo = p.c2p[cl(dlo)], chi = p.c2p[cl(dhi)];
-    const int plo = p.p2c[cl(dlo)], phi = p.p2c[cl(dhi)];
-    const bool far = clo == chi && plo == phi && (clo == 0 || clo == R - 1) && (plo == 0 || plo == R - 1);
-
-    bool kv_ok = true;
-    if (threadIdx.x < BN) {
-      const int j = j0 + threadIdx.x;
-      const bool in = j < sq.len;
-      const int64_t tj = sq.start + (in ? j : sq.len - 1);
-      const bool ok = in && (!p.kmask || p.kmask[tj]);
-      kb_s[threadIdx.x] = ok ? 0.f : -INFINITY;
-      kv_ok = ok;
-      if (far) bj_s[threadIdx.x] = TR::to_f(ends[(plo == 0 ? 2 : 3) * HT + int64_t(h) * T_ + tj]);
-    }
-    if (!far) {
-      for (int n = threadIdx.x; n < NL; n += 256) {
-        lutc[n] = p.c2p[cl(dlo + n)];
-        lutp[n] = p.p2c[cl(dlo + n)];
+    if constexpr (NARROW) {
+      if (cls == TILE_BAND) {
+        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
+        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
+                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
+        if (tid < BN) ps_s[tid] = lut_p(lut_s[buf][NL - 1 - tid]) & ~7;
+        __syncthreads();
       }
     }
-    const bool all_keys = __syncthreads_and(kv_ok);
-    const float a_far = clo == 0 ? a_end0 : a_end1;
 
-    float x[NKT][16];
+    float a = 0.f;
+    if (cls == TILE_FAR_LEFT) a = a_end1;
+    if (cls == TILE_FAR_RIGHT) a = a_end0;
+    const int cs = NARROW ? (lut_c(lut_s[buf][il]) & ~7) : 0;
+
+    float y[NKT][16];
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
       f32x16 acc = zero16();
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) acc = TR::mma(TR::ld(&Ks[(32 * t + li) * KP + q * KS + g * E]), Qf[q], acc);
+      for (int q = 0; q < NQ; ++q) acc = TR::mma(TR::ld(&Ks[buf][(32 * t + li) * KP + q * KS + g * E]), Qf[q], acc);
+      if (cls != TILE_BAND) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int jl = 32 * t + acc_row(v, g);
-        float val = acc[v] * p.scale_log2;
-        if (far) {
-          val += a_far + bj_s[jl];
-        } else {
-          const int n = (iw - i0) - jl + BN - 1;
-          const int jj = min(j0 + jl, sq.len - 1);
-          val += TR::to_f(c2prow[lutc[n]]) + TR::to_f(p2cbase[int64_t(jj) * RP + lutp[n]]);
+        for (int v = 0; v < 16; ++v) y[t][v] = fmaf(acc[v], p.scale_log2, bj_s[buf][32 * t + acc_row(v, g)]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int jl = 32 * t + acc_row(v, g);
+          const uint32_t e = lut_s[buf][il - jl + BN - 1];
+          float rel;
+          if constexpr (NARROW) {
+            rel = TR::to_f(Wc[il * WCP + lut_c(e) - cs]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps_s[jl]]);
+          } else {
+            const int jj = min(j0 + jl, sq.len - 1);
+            rel = TR::to_f(c2pstrip[int64_t(qin ? iw : sq.len - 1) * RP + lut_c(e)]) +
+                  TR::to_f(p2cstrip[int64_t(jj) * RP + lut_p(e)]);
+          }
+          y[t][v] = fmaf(acc[v], p.scale_log2, rel + bj_s[buf][jl]);
         }
-        if (!all_keys) val += kb_s[jl];
-        x[t][v] = val;
       }
     }
-    // online softmax (log2 domain)
+    // online softmax (log2 domain); a is this tile's per-row C2P value
     float mt = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, x[t][v]);
-    mt = fmaxf(mt, xor32(mt));
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, y[t][v]);
+    mt = fmaxf(mt, xor32(mt)) + a;
     const float mnew = fmaxf(m, mt);
     const float msafe = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = fast_exp2(m - msafe);
+    const float shift = msafe - a;
     float ls = 0.f;
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        x[t][v] = fast_exp2(x[t][v] - msafe);
-        ls += x[t][v];
+        y[t][v] = fast_exp2(y[t][v] - shift);
+        ls += y[t][v];
       }
     l = l * alpha + ls;
     m = mnew;
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd)
+      for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
+        for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
+    }
     // O^T += V^T P^T
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q) {
-        const frag pb = TR::pack(&x[t][q * E]);
+        const frag pb = TR::pack(&y[t][q * E]);
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
-          const T* vr = &Vt[(32 * nd + li) * VP + 32 * t];
+          const T* vr = &Vt[buf][(32 * nd + li) * VP + 32 * t];
           frag va;
           if constexpr (E == 8)
             va = TR::ld2x4(vr + 16 * q + 4 * g, vr + 16 * q + 8 + 4 * g);
@@ -165,6 +264,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(Params p) {
           O[nd] = TR::mma(va, pb, O[nd]);
         }
       }
+    if (kb + 1 < nkb) commit(buf ^ 1);
+    __syncthreads();
   }
 
   const float lt = l + xor32(l);
@@ -179,19 +280,27 @@ __global__ __launch_bounds__(256) void fwd_kernel(Params p) {
   if (g == 0) p.lse[int64_t(h) * T_ + tok_i] = ok ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NARROW>
 void launch_fwd_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
-  fwd_kernel<DT, D, NKT><<<grid, 256, 0, st>>>(p);
+  fwd_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
+}
+
+template <int DT, int D>
+void launch_fwd_n(const Params& p, hipStream_t st) {
+  if (p.narrow)
+    launch_fwd_d<DT, D, true>(p, st);
+  else
+    launch_fwd_d<DT, D, false>(p, st);
 }
 
 template <int DT>
 void launch_fwd_dt(const Params& p, hipStream_t st) {
   switch (p.D) {
-    case 32: launch_fwd_d<DT, 32>(p, st); break;
-    case 64: launch_fwd_d<DT, 64>(p, st); break;
-    default: launch_fwd_d<DT, 128>(p, st); break;
+    case 32: launch_fwd_n<DT, 32>(p, st); break;
+    case 64: launch_fwd_n<DT, 64>(p, st); break;
+    default: launch_fwd_n<DT, 128>(p, st); break;
   }
 }
 
