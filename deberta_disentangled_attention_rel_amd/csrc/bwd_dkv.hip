@@ -5,51 +5,60 @@
 // written once, by its owner, with no atomics.
 //
 // Work item: one sequence, one head, 128 keys (4 waves x 32 keys, resident
-// in registers). The loop walks 32*NQT queries at a time; Q, dO and their
-// transposes are staged in LDS. Each wave computes S = Q K^T and
+// in registers). The loop walks BM = 32*NQT queries at a time; the next query
+// tile (Q and dO rows and their transposes, per-query LSE/Delta/C2P-end
+// values, table slice) is loaded into registers during the current one and
+// written to LDS between two barriers. Each wave computes S = Q K^T and
 // dP = dO V^T with 32x32 MFMAs, so lane l owns key l % 32 and holds 16 of
-// every 32 queries. P = exp2(x - LSE*log2 e) is recomputed from the saved LSE,
-// dS = P (dP - Delta), and
-//   dV^T += dO^T P,   dK^T += Q^T dS       (accumulators lane-local per key)
+// every 32 queries:
+//   P = exp2(s log2e QK + rel - LSE log2e),  dS = P (dP - Delta)
+//   dV^T += dO^T P,   dK^T += Q^T dS
 //   dP2C[j, r] = sum_{i: delta(j,i) = r} dS[i, j]
-// The strip row of key j is owned by its lane and written by an ordered walk
-// over the queries; in far-field tiles (both index tables constant) the walk
-// takes the tile's column sum in one step. dK here is the dS^T Q part only;
-// the dP2C Q_r term is added by the relative-gradient GEMM.
-#include "tiles.hpp"
+// The strip row of key j is written by an ordered walk over the queries (one
+// step per tile in the far field). dK here is the dS^T Q part; the dP2C Q_r
+// term is added by the relative-gradient GEMM.
+#include "band.hpp"
 #include "walk.hpp"
 
 namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NQT>
-__global__ __launch_bounds__(256) void dkv_kernel(Params p) {
+template <int DT, int D, int NQT, bool NARROW>
+__global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
-  constexpr int BN = 128, BM = 32 * NQT;
+  constexpr int BN = 128, BM = 32 * NQT, NL = BM + BN - 1;
   constexpr int QP = Pitch<T, D>::rm, QTP = Pitch<T, BM>::tr;
-  constexpr int NL = BM + BN - 1;
+  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;   // C2P window: one row per query
+  constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;  // P2C window: one row per key
+  static_assert(NL <= 256, "one table entry per thread");
+  constexpr bool PAIR = sizeof(T) == 2;
+  constexpr int QIT = PAIR ? (BM / 2) * (D / CH) : BM * (D / CH), QPT = (QIT + 255) / 256;
 
   __shared__ __align__(16) T Qs[BM * QP];
   __shared__ __align__(16) T dOs[BM * QP];
   __shared__ __align__(16) T Qt[D * QTP];
   __shared__ __align__(16) T dOt[D * QTP];
-  __shared__ int lutc[NL], lutp[NL];
-  __shared__ __align__(16) float lse_s[BM];
+  __shared__ __align__(16) float uq_s[BM];   // per-query (C2P end) - LSE*log2e, -inf if masked
   __shared__ __align__(16) float dlt_s[BM];
-  __shared__ __align__(16) float aq_s[BM];
-  __shared__ __align__(16) float qok_s[BM];
+  __shared__ uint32_t lut_s[NL];
+  __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
+  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
+  __shared__ int cs_s[NARROW ? BM : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
   const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
   const int h = blockIdx.y;
   const int j0 = blockIdx.x * BN;
   if (j0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
-  const int R = p.R, RP = p.RP, off = p.Lmax - 1;
+  const int RP = p.RP;
+  const int d_hi = p.fbounds[0], d_lo = p.fbounds[1];
 
   const int jl = wave * 32 + li;  // this lane's key within the block
   const int jw = j0 + jl;
@@ -67,15 +76,97 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
       Vf[q] = TR::ld(vp + q * KS + g * E);
     }
   }
-  const T* ends = (const T*)p.ends;
-  const float b_end0 = TR::to_f(ends[2 * HT + int64_t(h) * T_ + tok_j]);
-  const float b_end1 = TR::to_f(ends[3 * HT + int64_t(h) * T_ + tok_j]);
-  const T* p2crow = (const T*)p.p2cs + (int64_t(h) * T_ + tok_j) * RP;
-  const T* c2pbase = (const T*)p.c2ps + (int64_t(h) * T_ + sq.start) * RP;
+  const T* ends = (const T*)p.ends + int64_t(h) * T_;
+  const float kbias = kvalid ? 0.f : -INFINITY;
+  const float b_end0 = TR::to_f(ends[2 * HT + tok_j]) + kbias;  // P2C column 0
+  const float b_end1 = TR::to_f(ends[3 * HT + tok_j]) + kbias;  // P2C column R-1
+  const T* c2pstrip = (const T*)p.c2ps + (int64_t(h) * T_ + sq.start) * RP;
+  const T* p2cstrip = (const T*)p.p2cs + (int64_t(h) * T_ + sq.start) * RP;
   const T* qbase = (const T*)p.q + sq.start * p.ts + int64_t(h) * p.hs;
   const T* dobase = (const T*)p.dout + sq.start * p.ts + int64_t(h) * p.hs;
   const float* lse = p.lse + int64_t(h) * T_ + sq.start;
   const float* dlt = p.delta + int64_t(h) * T_ + sq.start;
+  const uint8_t* kmask = p.kmask ? p.kmask + sq.start : nullptr;
+
+  auto cls_of = [&](int qb) {
+    const int i0 = qb * BM;
+    return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
+  };
+
+  uint4 qreg[QPT][PAIR ? 2 : 1], oreg[QPT][PAIR ? 2 : 1];
+  float ureg = 0.f, dreg = 0.f;
+  uint32_t lreg = 0;
+
+  auto load_rows = [&](uint4 (&dst)[QPT][PAIR ? 2 : 1], const T* base, int i0) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int it = tid + u * 256;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BM / 2)), c = (it / (BM / 2)) * CH;
+        dst[u][0] = dst[u][1] = make_uint4(0, 0, 0, 0);
+        if (it < QIT && i0 + r < sq.len) dst[u][0] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r) * p.ts + c);
+        if (it < QIT && i0 + r + 1 < sq.len)
+          dst[u][1] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r + 1) * p.ts + c);
+      } else {
+        const int r = it % BM, c = (it / BM) * CH;
+        dst[u][0] = make_uint4(0, 0, 0, 0);
+        if (it < QIT && i0 + r < sq.len) dst[u][0] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r) * p.ts + c);
+      }
+    }
+  };
+  auto store_rows = [&](const uint4 (&src)[QPT][PAIR ? 2 : 1], T* rm, T* tr) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int it = tid + u * 256;
+      if (it >= QIT) continue;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BM / 2)), c = (it / (BM / 2)) * CH;
+        *reinterpret_cast<uint4*>(&rm[r * QP + c]) = src[u][0];
+        *reinterpret_cast<uint4*>(&rm[(r + 1) * QP + c]) = src[u][1];
+        const uint32_t aw[4] = {src[u][0].x, src[u][0].y, src[u][0].z, src[u][0].w};
+        const uint32_t bw[4] = {src[u][1].x, src[u][1].y, src[u][1].z, src[u][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          *reinterpret_cast<uint32_t*>(&tr[(c + e) * QTP + r]) = lo | (hi << 16);
+        }
+      } else {
+        const int r = it % BM, c = (it / BM) * CH;
+        *reinterpret_cast<uint4*>(&rm[r * QP + c]) = src[u][0];
+        const float* f = reinterpret_cast<const float*>(&src[u][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(tr)[(c + e) * QTP + r] = f[e];
+      }
+    }
+  };
+
+  auto prefetch = [&](int qb) {
+    const int i0 = qb * BM;
+    const int cls = cls_of(qb);
+    load_rows(qreg, qbase, i0);
+    load_rows(oreg, dobase, i0);
+    if (tid < BM) {
+      const int i = i0 + tid;
+      const bool in = i < sq.len;
+      const int ic = in ? i : sq.len - 1;
+      const bool ok = in && (!kmask || kmask[ic]);
+      float a = 0.f;
+      if (cls != TILE_BAND) a = TR::to_f(ends[c2p_end_of(cls) * HT + sq.start + ic]);
+      ureg = ok ? a - lse[ic] * kLog2e : -INFINITY;
+      dreg = ok ? dlt[ic] : 0.f;
+    }
+    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+  };
+  auto commit = [&]() {
+    store_rows(qreg, Qs, Qt);
+    store_rows(oreg, dOs, dOt);
+    if (tid < BM) {
+      uq_s[tid] = ureg;
+      dlt_s[tid] = dreg;
+    }
+    if (tid < NL) lut_s[tid] = lreg;
+  };
 
   f32x16 dVt[ND], dKt[ND];
 #pragma unroll
@@ -84,40 +175,33 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
     dKt[nd] = zero16();
   }
   StripWalk<TR> walk;
-  walk.init((T*)p.dp2c + (int64_t(h) * T_ + tok_j) * RP, R, RP);
+  walk.init((T*)p.dp2c + (int64_t(h) * T_ + tok_j) * RP, p.R, RP);
   const bool walker = jin && g == 0;
 
   const int nqb = (sq.len + BM - 1) / BM;
+  prefetch(0);
+  commit();
+  __syncthreads();
+
   for (int qb = 0; qb < nqb; ++qb) {
     const int i0 = qb * BM;
-    __syncthreads();
-    stage_rows_tr<T, D, BM, QP, QTP, 256>(Qs, Qt, qbase, p.ts, i0, sq.len);
-    stage_rows_tr<T, D, BM, QP, QTP, 256>(dOs, dOt, dobase, p.ts, i0, sq.len);
-
-    const int dlo = i0 - (j0 + BN - 1), dhi = i0 + BM - 1 - j0;
-    auto cl = [&](int d) { return d < -off ? 0 : (d > off ? 2 * off : d + off); };
-    const int clo = p.c2p[cl(dlo)], chi = p.c2p[cl(dhi)];
-    const int plo = p.p2c[cl(dlo)], phi = p.p2c[cl(dhi)];
-    const bool far = clo == chi && plo == phi && (clo == 0 || clo == R - 1) && (plo == 0 || plo == R - 1);
-
-    if (threadIdx.x < BM) {
-      const int i = i0 + threadIdx.x;
-      const bool in = i < sq.len;
-      const int ic = in ? i : sq.len - 1;
-      const bool ok = in && (!p.kmask || p.kmask[sq.start + ic]);
-      qok_s[threadIdx.x] = ok ? 1.f : 0.f;
-      lse_s[threadIdx.x] = ok ? lse[ic] * kLog2e : 0.f;
-      dlt_s[threadIdx.x] = ok ? dlt[ic] : 0.f;
-      if (far) aq_s[threadIdx.x] = TR::to_f(ends[(clo == 0 ? 0 : 1) * HT + int64_t(h) * T_ + sq.start + ic]);
-    }
-    if (!far) {
-      for (int n = threadIdx.x; n < NL; n += 256) {
-        lutc[n] = p.c2p[cl(dlo + n)];
-        lutp[n] = p.p2c[cl(dlo + n)];
+    const int cls = cls_of(qb);
+    if constexpr (NARROW) {
+      if (cls == TILE_BAND) {
+        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+                                      [&](int r) { return lut_c(lut_s[r]) & ~7; });
+        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
+                                       [&](int r) { return lut_p(lut_s[NL - 1 - r]) & ~7; });
+        if (tid < BM) cs_s[tid] = lut_c(lut_s[tid]) & ~7;
+        __syncthreads();
       }
     }
-    __syncthreads();
-    const float b_far = plo == 0 ? b_end0 : b_end1;
+    if (qb + 1 < nqb) prefetch(qb + 1);
+
+    float bj = kbias;
+    if (cls == TILE_FAR_LEFT) bj = b_end0;
+    if (cls == TILE_FAR_RIGHT) bj = b_end1;
+    const int ps = NARROW ? (lut_p(lut_s[NL - 1 - jl]) & ~7) : 0;
 
     float colsum = 0.f;
 #pragma unroll
@@ -132,16 +216,18 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int il = 32 * u + acc_row(v, g);
-        float x = S[v] * p.scale_log2;
-        if (far) {
-          x += aq_s[il] + b_far;
-        } else {
-          const int n = il - jl + BN - 1;
-          const int ii = min(i0 + il, sq.len - 1);
-          x += TR::to_f(c2pbase[int64_t(ii) * RP + lutc[n]]) + TR::to_f(p2crow[lutp[n]]);
+        float rel = uq_s[il];
+        if (cls == TILE_BAND) {
+          const uint32_t e = lut_s[il - jl + BN - 1];
+          if constexpr (NARROW) {
+            rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs_s[il]]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps]);
+          } else {
+            const int ii = min(i0 + il, sq.len - 1);
+            rel += TR::to_f(c2pstrip[int64_t(ii) * RP + lut_c(e)]) +
+                   TR::to_f(p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)]);
+          }
         }
-        const bool ok = kvalid && qok_s[il] != 0.f;
-        P[v] = ok ? fast_exp2(x - lse_s[il]) : 0.f;
+        P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel) + bj);
         dS[v] = P[v] * (dP[v] - dlt_s[il]);
       }
 #pragma unroll
@@ -165,7 +251,7 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
         }
       }
       // dP2C: ordered walk over this subtile's queries
-      if (far) {
+      if (cls != TILE_BAND) {
         float cs = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) cs += dS[v];
@@ -180,12 +266,17 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
             const int il = 32 * u + k;
             if (i0 + il >= sq.len) break;
             const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lutp[il - jl + BN - 1], val);
+            walk.step(lut_p(lut_s[il - jl + BN - 1]), val);
           }
         }
       }
     }
-    if (far && walker) walk.step(plo, colsum);
+    if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? 0 : p.R - 1, colsum);
+    __syncthreads();
+    if (qb + 1 < nqb) {
+      commit();
+      __syncthreads();
+    }
   }
 
   if (!jin) return;
@@ -202,19 +293,27 @@ __global__ __launch_bounds__(256) void dkv_kernel(Params p) {
   if (g == 0) walk.finish();
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
-  constexpr int NQT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
-  dkv_kernel<DT, D, NQT><<<grid, 256, 0, st>>>(p);
+  constexpr int NQT = (DT == DF_FP32_T || D == 64) ? 1 : 2;
+  dkv_kernel<DT, D, NQT, NARROW><<<grid, 256, 0, st>>>(p);
+}
+
+template <int DT, int D>
+void launch_n(const Params& p, hipStream_t st) {
+  if (p.narrow)
+    launch_d<DT, D, true>(p, st);
+  else
+    launch_d<DT, D, false>(p, st);
 }
 
 template <int DT>
 void launch_dt(const Params& p, hipStream_t st) {
   switch (p.D) {
-    case 32: launch_d<DT, 32>(p, st); break;
-    case 64: launch_d<DT, 64>(p, st); break;
-    default: launch_d<DT, 128>(p, st); break;
+    case 32: launch_n<DT, 32>(p, st); break;
+    case 64: launch_n<DT, 64>(p, st); break;
+    default: launch_n<DT, 128>(p, st); break;
   }
 }
 

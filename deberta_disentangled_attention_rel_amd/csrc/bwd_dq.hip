@@ -3,45 +3,61 @@
 // "Performance": scores are recomputed in the backward).
 //
 // Work item: one sequence, one head, 128 queries (4 waves x 32 queries,
-// resident in registers). The loop walks 32*NKT keys at a time; K, V and K^T
-// are staged in LDS. Each wave computes S^T = K Q^T and dP^T = V dO^T, so lane
-// l owns query l % 32; P and dS are lane-local per query and
+// resident in registers). The loop walks BN = 32*NKT keys at a time; the next
+// tile (K rows and K^T, V rows, per-key P2C far-field values with the key
+// mask folded in, table slice) is loaded into registers during the current
+// one and written to LDS between two barriers. Each wave computes
+// S^T = K Q^T and dP^T = V dO^T, so lane l owns query l % 32; P and dS are
+// lane-local per query:
+//   P = exp2(s log2e QK + rel - LSE log2e),  dS = P (dP - Delta)
 //   dQ^T += K^T dS^T
 //   dC2P[i, r] = sum_{j: delta(i,j) = r} dS[i, j]
-// with the strip row of query i written by an ordered walk over the keys
-// (one step per tile in the far field). dQ here is the dS K part only; the
-// dC2P K_r term is added by the relative-gradient GEMM.
-#include "tiles.hpp"
+// The strip row of query i is written by an ordered walk over the keys (one
+// step per tile in the far field, where the whole tile shares one row). dQ
+// here is the dS K part; the dC2P K_r term is added by the relative-gradient
+// GEMM. No atomics.
+#include "band.hpp"
 #include "walk.hpp"
 
 namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NKT>
-__global__ __launch_bounds__(256) void dq_kernel(Params p) {
+template <int DT, int D, int NKT, bool NARROW>
+__global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
-  constexpr int BM = 128, BN = 32 * NKT;
+  constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
   constexpr int KP = Pitch<T, D>::rm, KTP = Pitch<T, BN>::tr;
-  constexpr int NL = BM + BN - 1;
+  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
+  constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
+  static_assert(NL <= 256, "one table entry per thread");
+  constexpr bool PAIR = sizeof(T) == 2;
+  // K rows: row pairs (16-bit) so the transposed copy is written in dwords
+  constexpr int KIT = PAIR ? (BN / 2) * (D / CH) : BN * (D / CH), KPT = (KIT + 255) / 256;
+  constexpr int VCH = BN * (D / CH), VPT = (VCH + 255) / 256;
 
   __shared__ __align__(16) T Ks[BN * KP];
   __shared__ __align__(16) T Vs[BN * KP];
   __shared__ __align__(16) T Kt[D * KTP];
-  __shared__ int lutc[NL], lutp[NL];
   __shared__ __align__(16) float bj_s[BN];
-  __shared__ __align__(16) float kb_s[BN];
+  __shared__ uint32_t lut_s[NL];
+  __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
+  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
+  __shared__ int ps_s[NARROW ? BN : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
   const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * BM;
   if (i0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
-  const int R = p.R, RP = p.RP, off = p.Lmax - 1;
+  const int R = p.R, RP = p.RP;
+  const int d_hi = p.fbounds[0], d_lo = p.fbounds[1];
 
   const int il = wave * 32 + li;
   const int iw = i0 + il;
@@ -59,15 +75,99 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
       dOf[q] = TR::ld(dp + q * KS + g * E);
     }
   }
-  const float lse2 = qvalid ? p.lse[int64_t(h) * T_ + tok_i] * kLog2e : 0.f;
+  // masked query: P = 0 through an infinite LSE
+  const float lse2 = qvalid ? p.lse[int64_t(h) * T_ + tok_i] * kLog2e : INFINITY;
   const float dlt = qvalid ? p.delta[int64_t(h) * T_ + tok_i] : 0.f;
-  const T* ends = (const T*)p.ends;
-  const float a_end0 = TR::to_f(ends[int64_t(h) * T_ + tok_i]);
-  const float a_end1 = TR::to_f(ends[HT + int64_t(h) * T_ + tok_i]);
-  const T* c2prow = (const T*)p.c2ps + (int64_t(h) * T_ + tok_i) * RP;
-  const T* p2cbase = (const T*)p.p2cs + (int64_t(h) * T_ + sq.start) * RP;
+  const T* ends = (const T*)p.ends + int64_t(h) * T_;
+  const float a_end0 = TR::to_f(ends[tok_i]);
+  const float a_end1 = TR::to_f(ends[HT + tok_i]);
+  const T* c2pstrip = (const T*)p.c2ps + (int64_t(h) * T_ + sq.start) * RP;
+  const T* p2cstrip = (const T*)p.p2cs + (int64_t(h) * T_ + sq.start) * RP;
   const T* kbase = (const T*)p.k + sq.start * p.ts + int64_t(h) * p.hs;
   const T* vbase = (const T*)p.v + sq.start * p.ts + int64_t(h) * p.hs;
+  const uint8_t* kmask = p.kmask ? p.kmask + sq.start : nullptr;
+
+  auto cls_of = [&](int kb) {
+    const int j0 = kb * BN;
+    return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
+  };
+
+  uint4 kreg[KPT][PAIR ? 2 : 1];
+  uint4 vreg[VPT];
+  float breg = 0.f;
+  uint32_t lreg = 0;
+
+  auto prefetch = [&](int kb) {
+    const int j0 = kb * BN;
+    const int cls = cls_of(kb);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = tid + u * 256;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
+        kreg[u][0] = kreg[u][1] = make_uint4(0, 0, 0, 0);
+        if (it < KIT && j0 + r < sq.len) kreg[u][0] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
+        if (it < KIT && j0 + r + 1 < sq.len)
+          kreg[u][1] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r + 1) * p.ts + c);
+      } else {
+        const int r = it % BN, c = (it / BN) * CH;
+        kreg[u][0] = make_uint4(0, 0, 0, 0);
+        if (it < KIT && j0 + r < sq.len) kreg[u][0] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = tid + u * 256;
+      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
+      vreg[u] = make_uint4(0, 0, 0, 0);
+      if (it < VCH && j0 + r < sq.len) vreg[u] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
+    }
+    if (tid < BN) {
+      const int j = j0 + tid;
+      const bool in = j < sq.len;
+      const int jc = in ? j : sq.len - 1;
+      const bool ok = in && (!kmask || kmask[jc]);
+      float b = 0.f;
+      if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
+      breg = ok ? b : -INFINITY;
+    }
+    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+  };
+
+  auto commit = [&]() {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = tid + u * 256;
+      if (it >= KIT) continue;
+      if constexpr (PAIR) {
+        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
+        *reinterpret_cast<uint4*>(&Ks[r * KP + c]) = kreg[u][0];
+        *reinterpret_cast<uint4*>(&Ks[(r + 1) * KP + c]) = kreg[u][1];
+        const uint32_t aw[4] = {kreg[u][0].x, kreg[u][0].y, kreg[u][0].z, kreg[u][0].w};
+        const uint32_t bw[4] = {kreg[u][1].x, kreg[u][1].y, kreg[u][1].z, kreg[u][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          *reinterpret_cast<uint32_t*>(&Kt[(c + e) * KTP + r]) = lo | (hi << 16);
+        }
+      } else {
+        const int r = it % BN, c = (it / BN) * CH;
+        *reinterpret_cast<uint4*>(&Ks[r * KP + c]) = kreg[u][0];
+        const float* f = reinterpret_cast<const float*>(&kreg[u][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(Kt)[(c + e) * KTP + r] = f[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = tid + u * 256;
+      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
+      if (it < VCH) *reinterpret_cast<uint4*>(&Vs[r * KP + c]) = vreg[u];
+    }
+    if (tid < BN) bj_s[tid] = breg;
+    if (tid < NL) lut_s[tid] = lreg;
+  };
 
   f32x16 dQt[ND];
 #pragma unroll
@@ -77,36 +177,30 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   const bool walker = qin && g == 0;
 
   const int nkb = (sq.len + BN - 1) / BN;
+  prefetch(0);
+  commit();
+  __syncthreads();
+
   for (int kb = 0; kb < nkb; ++kb) {
     const int j0 = kb * BN;
-    __syncthreads();
-    stage_rows_tr<T, D, BN, KP, KTP, 256>(Ks, Kt, kbase, p.ts, j0, sq.len);
-    stage_rows<T, D, BN, KP, 256>(Vs, vbase, p.ts, j0, sq.len);
-
-    const int dlo = i0 - (j0 + BN - 1), dhi = i0 + BM - 1 - j0;
-    auto cl = [&](int d) { return d < -off ? 0 : (d > off ? 2 * off : d + off); };
-    const int clo = p.c2p[cl(dlo)], chi = p.c2p[cl(dhi)];
-    const int plo = p.p2c[cl(dlo)], phi = p.p2c[cl(dhi)];
-    const bool far = clo == chi && plo == phi && (clo == 0 || clo == R - 1) && (plo == 0 || plo == R - 1);
-
-    bool kv_ok = true;
-    if (threadIdx.x < BN) {
-      const int j = j0 + threadIdx.x;
-      const bool in = j < sq.len;
-      const int64_t tj = sq.start + (in ? j : sq.len - 1);
-      const bool ok = in && (!p.kmask || p.kmask[tj]);
-      kb_s[threadIdx.x] = ok ? 0.f : -INFINITY;
-      kv_ok = ok;
-      if (far) bj_s[threadIdx.x] = TR::to_f(ends[(plo == 0 ? 2 : 3) * HT + int64_t(h) * T_ + tj]);
-    }
-    if (!far) {
-      for (int n = threadIdx.x; n < NL; n += 256) {
-        lutc[n] = p.c2p[cl(dlo + n)];
-        lutp[n] = p.p2c[cl(dlo + n)];
+    const int cls = cls_of(kb);
+    if constexpr (NARROW) {
+      if (cls == TILE_BAND) {
+        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+                                      [&](int r) { return lut_c(lut_s[r]) & ~7; });
+        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
+                                       [&](int r) { return lut_p(lut_s[NL - 1 - r]) & ~7; });
+        if (tid < BN) ps_s[tid] = lut_p(lut_s[NL - 1 - tid]) & ~7;
+        __syncthreads();
       }
     }
-    const bool all_keys = __syncthreads_and(kv_ok);
-    const float a_far = clo == 0 ? a_end0 : a_end1;
+    if (kb + 1 < nkb) prefetch(kb + 1);
+
+    float a = 0.f;
+    if (cls == TILE_FAR_LEFT) a = a_end1;
+    if (cls == TILE_FAR_RIGHT) a = a_end0;
+    const float w = a - lse2;
+    const int cs = NARROW ? (lut_c(lut_s[il]) & ~7) : 0;
 
     float rowsum = 0.f;
 #pragma unroll
@@ -121,16 +215,18 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int jl = 32 * t + acc_row(v, g);
-        float x = S[v] * p.scale_log2;
-        if (far) {
-          x += a_far + bj_s[jl];
-        } else {
-          const int n = il - jl + BN - 1;
-          const int jj = min(j0 + jl, sq.len - 1);
-          x += TR::to_f(c2prow[lutc[n]]) + TR::to_f(p2cbase[int64_t(jj) * RP + lutp[n]]);
+        float rel = bj_s[jl];
+        if (cls == TILE_BAND) {
+          const uint32_t e = lut_s[il - jl + BN - 1];
+          if constexpr (NARROW) {
+            rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps_s[jl]]);
+          } else {
+            const int jj = min(j0 + jl, sq.len - 1);
+            rel += TR::to_f(c2pstrip[int64_t(qin ? iw : sq.len - 1) * RP + lut_c(e)]) +
+                   TR::to_f(p2cstrip[int64_t(jj) * RP + lut_p(e)]);
+          }
         }
-        if (!all_keys) x += kb_s[jl];
-        const float P = qvalid ? fast_exp2(x - lse2) : 0.f;
+        const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel) + w);
         dS[v] = P * (dP[v] - dlt);
       }
 #pragma unroll
@@ -139,16 +235,16 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
           const T* kr = &Kt[(32 * nd + li) * KTP + 32 * t];
-          frag a;
+          frag am;
           if constexpr (E == 8)
-            a = TR::ld2x4(kr + 16 * q + 4 * g, kr + 16 * q + 8 + 4 * g);
+            am = TR::ld2x4(kr + 16 * q + 4 * g, kr + 16 * q + 8 + 4 * g);
           else
-            a = TR::ld(kr + fed_row<E>(q, 0, g));
-          dQt[nd] = TR::mma(a, sb, dQt[nd]);
+            am = TR::ld(kr + fed_row<E>(q, 0, g));
+          dQt[nd] = TR::mma(am, sb, dQt[nd]);
         }
       }
       // dC2P: ordered walk over this subtile's keys
-      if (far) {
+      if (cls != TILE_BAND) {
         float rs = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) rs += dS[v];
@@ -163,12 +259,17 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
             const int jl = 32 * t + k;
             if (j0 + jl >= sq.len) break;
             const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lutc[il - jl + BN - 1], val);
+            walk.step(lut_c(lut_s[il - jl + BN - 1]), val);
           }
         }
       }
     }
-    if (far && walker) walk.step(clo, rowsum);
+    if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+    __syncthreads();
+    if (kb + 1 < nkb) {
+      commit();
+      __syncthreads();
+    }
   }
 
   if (!qin) return;
@@ -180,19 +281,27 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   if (g == 0) walk.finish();
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
-  dq_kernel<DT, D, NKT><<<grid, 256, 0, st>>>(p);
+  dq_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
+}
+
+template <int DT, int D>
+void launch_n(const Params& p, hipStream_t st) {
+  if (p.narrow)
+    launch_d<DT, D, true>(p, st);
+  else
+    launch_d<DT, D, false>(p, st);
 }
 
 template <int DT>
 void launch_dt(const Params& p, hipStream_t st) {
   switch (p.D) {
-    case 32: launch_d<DT, 32>(p, st); break;
-    case 64: launch_d<DT, 64>(p, st); break;
-    default: launch_d<DT, 128>(p, st); break;
+    case 32: launch_n<DT, 32>(p, st); break;
+    case 64: launch_n<DT, 64>(p, st); break;
+    default: launch_n<DT, 128>(p, st); break;
   }
 }
 

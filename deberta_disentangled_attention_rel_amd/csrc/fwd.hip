@@ -27,7 +27,7 @@ namespace dfa {
 namespace {
 
 template <int DT, int D, int NKT, bool NARROW>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(Params p) {
+__global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
