@@ -6,9 +6,10 @@
 //
 // Work item: one sequence, one head, 128 keys (4 waves x 32 keys, resident
 // in registers). The loop walks BM = 32*NQT queries at a time; the next query
-// tile (Q and dO rows and their transposes, per-query LSE/Delta/C2P-end
-// values, table slice) is loaded into registers during the current one and
-// written to LDS between two barriers. Each wave computes S = Q K^T and
+// tile (Q and dO rows, per-query LSE/Delta/C2P-end values, table slice) is
+// loaded into registers during the current one and written to the other half
+// of a double-buffered LDS area (one barrier per tile); the Q^T and dO^T
+// operands are read with transposing LDS reads. Each wave computes S = Q K^T and
 // dP = dO V^T with 32x32 MFMAs, so lane l owns key l % 32 and holds 16 of
 // every 32 queries:
 //   P = exp2(s log2e QK + rel - LSE log2e),  dS = P (dP - Delta)
@@ -18,6 +19,7 @@
 // step per tile in the far field). dK here is the dS^T Q part; the dP2C Q_r
 // term is added by the relative-gradient GEMM.
 #include "band.hpp"
+#include "pipe.hpp"
 #include "walk.hpp"
 
 namespace dfa {
@@ -31,21 +33,17 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
   constexpr int BN = 128, BM = 32 * NQT, NL = BM + BN - 1;
-  constexpr int QP = Pitch<T, D>::rm, QTP = Pitch<T, BM>::tr;
-  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int QP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;   // C2P window: one row per query
   constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;  // P2C window: one row per key
   static_assert(NL <= 256, "one table entry per thread");
-  constexpr bool PAIR = sizeof(T) == 2;
-  constexpr int QIT = PAIR ? (BM / 2) * (D / CH) : BM * (D / CH), QPT = (QIT + 255) / 256;
+  using QTile = RowTile<T, BM, D, 256>;
 
-  __shared__ __align__(16) T Qs[BM * QP];
-  __shared__ __align__(16) T dOs[BM * QP];
-  __shared__ __align__(16) T Qt[D * QTP];
-  __shared__ __align__(16) T dOt[D * QTP];
-  __shared__ __align__(16) float uq_s[BM];   // per-query (C2P end) - LSE*log2e, -inf if masked
-  __shared__ __align__(16) float dlt_s[BM];
-  __shared__ uint32_t lut_s[NL];
+  __shared__ __align__(16) T Qs[2][BM * QP];
+  __shared__ __align__(16) T dOs[2][BM * QP];
+  __shared__ __align__(16) float uq_s[2][BM];   // per-query (C2P end) - LSE*log2e, -inf if masked
+  __shared__ __align__(16) float dlt_s[2][BM];
+  __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
   __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
   __shared__ int cs_s[NARROW ? BM : 1];
@@ -93,59 +91,17 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
   };
 
-  uint4 qreg[QPT][PAIR ? 2 : 1], oreg[QPT][PAIR ? 2 : 1];
+  QTile qt, ot;
+  qt.init();
+  ot.init();
   float ureg = 0.f, dreg = 0.f;
   uint32_t lreg = 0;
-
-  auto load_rows = [&](uint4 (&dst)[QPT][PAIR ? 2 : 1], const T* base, int i0) {
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int it = tid + u * 256;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BM / 2)), c = (it / (BM / 2)) * CH;
-        dst[u][0] = dst[u][1] = make_uint4(0, 0, 0, 0);
-        if (it < QIT && i0 + r < sq.len) dst[u][0] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r) * p.ts + c);
-        if (it < QIT && i0 + r + 1 < sq.len)
-          dst[u][1] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r + 1) * p.ts + c);
-      } else {
-        const int r = it % BM, c = (it / BM) * CH;
-        dst[u][0] = make_uint4(0, 0, 0, 0);
-        if (it < QIT && i0 + r < sq.len) dst[u][0] = *reinterpret_cast<const uint4*>(base + int64_t(i0 + r) * p.ts + c);
-      }
-    }
-  };
-  auto store_rows = [&](const uint4 (&src)[QPT][PAIR ? 2 : 1], T* rm, T* tr) {
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int it = tid + u * 256;
-      if (it >= QIT) continue;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BM / 2)), c = (it / (BM / 2)) * CH;
-        *reinterpret_cast<uint4*>(&rm[r * QP + c]) = src[u][0];
-        *reinterpret_cast<uint4*>(&rm[(r + 1) * QP + c]) = src[u][1];
-        const uint32_t aw[4] = {src[u][0].x, src[u][0].y, src[u][0].z, src[u][0].w};
-        const uint32_t bw[4] = {src[u][1].x, src[u][1].y, src[u][1].z, src[u][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(&tr[(c + e) * QTP + r]) = lo | (hi << 16);
-        }
-      } else {
-        const int r = it % BM, c = (it / BM) * CH;
-        *reinterpret_cast<uint4*>(&rm[r * QP + c]) = src[u][0];
-        const float* f = reinterpret_cast<const float*>(&src[u][0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(tr)[(c + e) * QTP + r] = f[e];
-      }
-    }
-  };
 
   auto prefetch = [&](int qb) {
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
-    load_rows(qreg, qbase, i0);
-    load_rows(oreg, dobase, i0);
+    qt.load(qbase, p.ts, i0, sq.len);
+    ot.load(dobase, p.ts, i0, sq.len);
     if (tid < BM) {
       const int i = i0 + tid;
       const bool in = i < sq.len;
@@ -158,14 +114,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     }
     if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
-  auto commit = [&]() {
-    store_rows(qreg, Qs, Qt);
-    store_rows(oreg, dOs, dOt);
+  auto commit = [&](int buf) {
+    qt.template store<QP>(Qs[buf]);
+    ot.template store<QP>(dOs[buf]);
     if (tid < BM) {
-      uq_s[tid] = ureg;
-      dlt_s[tid] = dreg;
+      uq_s[buf][tid] = ureg;
+      dlt_s[buf][tid] = dreg;
     }
-    if (tid < NL) lut_s[tid] = lreg;
+    if (tid < NL) lut_s[buf][tid] = lreg;
   };
 
   f32x16 dVt[ND], dKt[ND];
@@ -180,28 +136,29 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 
   const int nqb = (sq.len + BM - 1) / BM;
   prefetch(0);
-  commit();
+  commit(0);
   __syncthreads();
 
   for (int qb = 0; qb < nqb; ++qb) {
+    const int buf = qb & 1;
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
+    if (qb + 1 < nqb) prefetch(qb + 1);
     if constexpr (NARROW) {
       if (cls == TILE_BAND) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return lut_c(lut_s[r]) & ~7; });
+                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
         stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return lut_p(lut_s[NL - 1 - r]) & ~7; });
-        if (tid < BM) cs_s[tid] = lut_c(lut_s[tid]) & ~7;
+                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
+        if (tid < BM) cs_s[tid] = lut_c(lut_s[buf][tid]) & ~7;
         __syncthreads();
       }
     }
-    if (qb + 1 < nqb) prefetch(qb + 1);
 
     float bj = kbias;
     if (cls == TILE_FAR_LEFT) bj = b_end0;
     if (cls == TILE_FAR_RIGHT) bj = b_end1;
-    const int ps = NARROW ? (lut_p(lut_s[NL - 1 - jl]) & ~7) : 0;
+    const int ps = NARROW ? (lut_p(lut_s[buf][NL - 1 - jl]) & ~7) : 0;
 
     float colsum = 0.f;
 #pragma unroll
@@ -209,16 +166,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       f32x16 S = zero16(), dP = zero16();
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        S = TR::mma(TR::ld(&Qs[(32 * u + li) * QP + q * KS + g * E]), Kf[q], S);
-        dP = TR::mma(TR::ld(&dOs[(32 * u + li) * QP + q * KS + g * E]), Vf[q], dP);
+        S = TR::mma(ld_row<TR>(Qs[buf], QP, 32 * u + li, q * KS + g * E), Kf[q], S);
+        dP = TR::mma(ld_row<TR>(dOs[buf], QP, 32 * u + li, q * KS + g * E), Vf[q], dP);
       }
       float P[16], dS[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int il = 32 * u + acc_row(v, g);
-        float rel = uq_s[il];
+        float rel = uq_s[buf][il];
         if (cls == TILE_BAND) {
-          const uint32_t e = lut_s[il - jl + BN - 1];
+          const uint32_t e = lut_s[buf][il - jl + BN - 1];
           if constexpr (NARROW) {
             rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs_s[il]]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps]);
           } else {
@@ -228,7 +185,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           }
         }
         P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel) + bj);
-        dS[v] = P[v] * (dP[v] - dlt_s[il]);
+        dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
       }
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q) {
@@ -236,18 +193,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         const frag sb = TR::pack(&dS[q * E]);
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
-          const T* dr = &dOt[(32 * nd + li) * QTP + 32 * u];
-          const T* qr = &Qt[(32 * nd + li) * QTP + 32 * u];
-          frag a_do, a_q;
-          if constexpr (E == 8) {
-            a_do = TR::ld2x4(dr + 16 * q + 4 * g, dr + 16 * q + 8 + 4 * g);
-            a_q = TR::ld2x4(qr + 16 * q + 4 * g, qr + 16 * q + 8 + 4 * g);
-          } else {
-            a_do = TR::ld(dr + fed_row<E>(q, 0, g));
-            a_q = TR::ld(qr + fed_row<E>(q, 0, g));
-          }
-          dVt[nd] = TR::mma(a_do, pb, dVt[nd]);
-          dKt[nd] = TR::mma(a_q, sb, dKt[nd]);
+          dVt[nd] = TR::mma(ld_col<TR>(dOs[buf], QP, 32 * u, 32 * nd, q), pb, dVt[nd]);
+          dKt[nd] = TR::mma(ld_col<TR>(Qs[buf], QP, 32 * u, 32 * nd, q), sb, dKt[nd]);
         }
       }
       // dP2C: ordered walk over this subtile's queries
@@ -266,17 +213,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
             const int il = 32 * u + k;
             if (i0 + il >= sq.len) break;
             const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lut_p(lut_s[il - jl + BN - 1]), val);
+            walk.step(lut_p(lut_s[buf][il - jl + BN - 1]), val);
           }
         }
       }
     }
     if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? 0 : p.R - 1, colsum);
+    if (qb + 1 < nqb) commit(buf ^ 1);
     __syncthreads();
-    if (qb + 1 < nqb) {
-      commit();
-      __syncthreads();
-    }
   }
 
   if (!jin) return;
@@ -296,7 +240,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
-  constexpr int NQT = (DT == DF_FP32_T || D == 64) ? 1 : 2;
+  constexpr int NQT = (DT == DF_FP32_T) ? 1 : 2;
   dkv_kernel<DT, D, NQT, NARROW><<<grid, 256, 0, st>>>(p);
 }
 

@@ -4,9 +4,10 @@
 //
 // Work item: one sequence, one head, 128 queries (4 waves x 32 queries,
 // resident in registers). The loop walks BN = 32*NKT keys at a time; the next
-// tile (K rows and K^T, V rows, per-key P2C far-field values with the key
-// mask folded in, table slice) is loaded into registers during the current
-// one and written to LDS between two barriers. Each wave computes
+// tile (K and V rows, per-key P2C far-field values with the key mask folded
+// in, table slice) is loaded into registers during the current one and
+// written to the other half of a double-buffered LDS area (one barrier per
+// tile); the K^T operand is read with transposing LDS reads. Each wave computes
 // S^T = K Q^T and dP^T = V dO^T, so lane l owns query l % 32; P and dS are
 // lane-local per query:
 //   P = exp2(s log2e QK + rel - LSE log2e),  dS = P (dP - Delta)
@@ -17,6 +18,7 @@
 // here is the dS K part; the dC2P K_r term is added by the relative-gradient
 // GEMM. No atomics.
 #include "band.hpp"
+#include "pipe.hpp"
 #include "walk.hpp"
 
 namespace dfa {
@@ -30,21 +32,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
   constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
-  constexpr int KP = Pitch<T, D>::rm, KTP = Pitch<T, BN>::tr;
-  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int KP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
   constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
   static_assert(NL <= 256, "one table entry per thread");
-  constexpr bool PAIR = sizeof(T) == 2;
-  // K rows: row pairs (16-bit) so the transposed copy is written in dwords
-  constexpr int KIT = PAIR ? (BN / 2) * (D / CH) : BN * (D / CH), KPT = (KIT + 255) / 256;
-  constexpr int VCH = BN * (D / CH), VPT = (VCH + 255) / 256;
+  using KTile = RowTile<T, BN, D, 256>;
 
-  __shared__ __align__(16) T Ks[BN * KP];
-  __shared__ __align__(16) T Vs[BN * KP];
-  __shared__ __align__(16) T Kt[D * KTP];
-  __shared__ __align__(16) float bj_s[BN];
-  __shared__ uint32_t lut_s[NL];
+  __shared__ __align__(16) T Ks[2][BN * KP];
+  __shared__ __align__(16) T Vs[2][BN * KP];
+  __shared__ __align__(16) float bj_s[2][BN];
+  __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
   __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
   __shared__ int ps_s[NARROW ? BN : 1];
@@ -92,36 +89,17 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
   };
 
-  uint4 kreg[KPT][PAIR ? 2 : 1];
-  uint4 vreg[VPT];
+  KTile kt, vt;
+  kt.init();
+  vt.init();
   float breg = 0.f;
   uint32_t lreg = 0;
 
   auto prefetch = [&](int kb) {
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int it = tid + u * 256;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
-        kreg[u][0] = kreg[u][1] = make_uint4(0, 0, 0, 0);
-        if (it < KIT && j0 + r < sq.len) kreg[u][0] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
-        if (it < KIT && j0 + r + 1 < sq.len)
-          kreg[u][1] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r + 1) * p.ts + c);
-      } else {
-        const int r = it % BN, c = (it / BN) * CH;
-        kreg[u][0] = make_uint4(0, 0, 0, 0);
-        if (it < KIT && j0 + r < sq.len) kreg[u][0] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int it = tid + u * 256;
-      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
-      vreg[u] = make_uint4(0, 0, 0, 0);
-      if (it < VCH && j0 + r < sq.len) vreg[u] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
-    }
+    kt.load(kbase, p.ts, j0, sq.len);
+    vt.load(vbase, p.ts, j0, sq.len);
     if (tid < BN) {
       const int j = j0 + tid;
       const bool in = j < sq.len;
@@ -134,39 +112,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
 
-  auto commit = [&]() {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int it = tid + u * 256;
-      if (it >= KIT) continue;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
-        *reinterpret_cast<uint4*>(&Ks[r * KP + c]) = kreg[u][0];
-        *reinterpret_cast<uint4*>(&Ks[(r + 1) * KP + c]) = kreg[u][1];
-        const uint32_t aw[4] = {kreg[u][0].x, kreg[u][0].y, kreg[u][0].z, kreg[u][0].w};
-        const uint32_t bw[4] = {kreg[u][1].x, kreg[u][1].y, kreg[u][1].z, kreg[u][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(&Kt[(c + e) * KTP + r]) = lo | (hi << 16);
-        }
-      } else {
-        const int r = it % BN, c = (it / BN) * CH;
-        *reinterpret_cast<uint4*>(&Ks[r * KP + c]) = kreg[u][0];
-        const float* f = reinterpret_cast<const float*>(&kreg[u][0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(Kt)[(c + e) * KTP + r] = f[e];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int it = tid + u * 256;
-      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
-      if (it < VCH) *reinterpret_cast<uint4*>(&Vs[r * KP + c]) = vreg[u];
-    }
-    if (tid < BN) bj_s[tid] = breg;
-    if (tid < NL) lut_s[tid] = lreg;
+  auto commit = [&](int buf) {
+    kt.template store<KP>(Ks[buf]);
+    vt.template store<KP>(Vs[buf]);
+    if (tid < BN) bj_s[buf][tid] = breg;
+    if (tid < NL) lut_s[buf][tid] = lreg;
   };
 
   f32x16 dQt[ND];
@@ -178,29 +128,30 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 
   const int nkb = (sq.len + BN - 1) / BN;
   prefetch(0);
-  commit();
+  commit(0);
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
+    if (kb + 1 < nkb) prefetch(kb + 1);
     if constexpr (NARROW) {
       if (cls == TILE_BAND) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return lut_c(lut_s[r]) & ~7; });
+                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
         stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return lut_p(lut_s[NL - 1 - r]) & ~7; });
-        if (tid < BN) ps_s[tid] = lut_p(lut_s[NL - 1 - tid]) & ~7;
+                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
+        if (tid < BN) ps_s[tid] = lut_p(lut_s[buf][NL - 1 - tid]) & ~7;
         __syncthreads();
       }
     }
-    if (kb + 1 < nkb) prefetch(kb + 1);
 
     float a = 0.f;
     if (cls == TILE_FAR_LEFT) a = a_end1;
     if (cls == TILE_FAR_RIGHT) a = a_end0;
     const float w = a - lse2;
-    const int cs = NARROW ? (lut_c(lut_s[il]) & ~7) : 0;
+    const int cs = NARROW ? (lut_c(lut_s[buf][il]) & ~7) : 0;
 
     float rowsum = 0.f;
 #pragma unroll
@@ -208,16 +159,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
       f32x16 S = zero16(), dP = zero16();
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        S = TR::mma(TR::ld(&Ks[(32 * t + li) * KP + q * KS + g * E]), Qf[q], S);
-        dP = TR::mma(TR::ld(&Vs[(32 * t + li) * KP + q * KS + g * E]), dOf[q], dP);
+        S = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], S);
+        dP = TR::mma(ld_row<TR>(Vs[buf], KP, 32 * t + li, q * KS + g * E), dOf[q], dP);
       }
       float dS[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int jl = 32 * t + acc_row(v, g);
-        float rel = bj_s[jl];
+        float rel = bj_s[buf][jl];
         if (cls == TILE_BAND) {
-          const uint32_t e = lut_s[il - jl + BN - 1];
+          const uint32_t e = lut_s[buf][il - jl + BN - 1];
           if constexpr (NARROW) {
             rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps_s[jl]]);
           } else {
@@ -233,15 +184,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
       for (int q = 0; q < 32 / KS; ++q) {
         const frag sb = TR::pack(&dS[q * E]);
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const T* kr = &Kt[(32 * nd + li) * KTP + 32 * t];
-          frag am;
-          if constexpr (E == 8)
-            am = TR::ld2x4(kr + 16 * q + 4 * g, kr + 16 * q + 8 + 4 * g);
-          else
-            am = TR::ld(kr + fed_row<E>(q, 0, g));
-          dQt[nd] = TR::mma(am, sb, dQt[nd]);
-        }
+        for (int nd = 0; nd < ND; ++nd) dQt[nd] = TR::mma(ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q), sb, dQt[nd]);
       }
       // dC2P: ordered walk over this subtile's keys
       if (cls != TILE_BAND) {
@@ -259,17 +202,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
             const int jl = 32 * t + k;
             if (j0 + jl >= sq.len) break;
             const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lut_c(lut_s[il - jl + BN - 1]), val);
+            walk.step(lut_c(lut_s[buf][il - jl + BN - 1]), val);
           }
         }
       }
     }
     if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+    if (kb + 1 < nkb) commit(buf ^ 1);
     __syncthreads();
-    if (kb + 1 < nkb) {
-      commit();
-      __syncthreads();
-    }
   }
 
   if (!qin) return;

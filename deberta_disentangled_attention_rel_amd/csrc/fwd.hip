@@ -3,11 +3,12 @@
 // usage": the LSE-producing training forward).
 //
 // Work item: one sequence, one head, 128 query rows (4 waves x 32). The key
-// loop walks BN = 32*NKT keys at a time. The next key tile (K rows, V rows
-// transposed, per-key P2C far-field values with the key mask folded in, and
-// the index-table slice) is loaded into registers while the current one is
+// loop walks BN = 32*NKT keys at a time. The next key tile (K rows, V rows,
+// per-key P2C far-field values with the key mask folded in, and the
+// index-table slice) is loaded into registers while the current one is
 // computed, then written to the other half of a double-buffered LDS area:
-// one barrier per tile.
+// one barrier per tile. Both tiles stay row-major; the V^T operand is read
+// with transposing LDS reads.
 //
 // Each wave computes S^T = K Q^T with 32x32 MFMAs, so lane l owns query row
 // l % 32 and holds 16 of every 32 keys (the other 16 sit in lane l ^ 32).
@@ -21,6 +22,7 @@
 // band tile stages the strip windows it needs in LDS and gathers both terms
 // per pair from there (or from global memory when the tables can skip rows).
 #include "band.hpp"
+#include "pipe.hpp"
 
 namespace dfa {
 
@@ -33,18 +35,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
   constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
-  constexpr int KP = Pitch<T, D>::rm, VP = Pitch<T, BN>::tr;
-  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int KP = RowPitch<T, D>::rows, VP = RowPitch<T, D>::cols;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
   constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
   static_assert(NL <= 256, "one table entry per thread");
-  // prefetch shapes: K rows as 16-byte chunks; V rows as (16-bit) row pairs
-  constexpr int KCH = BN * (D / CH), KPT = (KCH + 255) / 256;
-  constexpr bool PAIR = sizeof(T) == 2;
-  constexpr int VIT = PAIR ? (BN / 2) * (D / CH) : BN * (D / CH), VPT = (VIT + 255) / 256;
+  using KTile = RowTile<T, BN, D, 256>;
 
   __shared__ __align__(16) T Ks[2][BN * KP];
-  __shared__ __align__(16) T Vt[2][D * VP];
+  __shared__ __align__(16) T Vs[2][BN * VP];
   __shared__ __align__(16) float bj_s[2][BN];
   __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
@@ -88,36 +86,17 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   };
 
   // ---- next-tile registers
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][PAIR ? 2 : 1];
+  KTile kt, vt;
+  kt.init();
+  vt.init();
   float breg = 0.f;
   uint32_t lreg = 0;
 
   auto prefetch = [&](int kb) {
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int it = tid + u * 256;
-      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
-      kreg[u] = make_uint4(0, 0, 0, 0);
-      if (it < KCH && j0 + r < sq.len) kreg[u] = *reinterpret_cast<const uint4*>(kbase + int64_t(j0 + r) * p.ts + c);
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int it = tid + u * 256;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
-        vreg[u][0] = vreg[u][1] = make_uint4(0, 0, 0, 0);
-        if (it < VIT && j0 + r < sq.len) vreg[u][0] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
-        if (it < VIT && j0 + r + 1 < sq.len)
-          vreg[u][1] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r + 1) * p.ts + c);
-      } else {
-        const int r = it % BN, c = (it / BN) * CH;
-        vreg[u][0] = make_uint4(0, 0, 0, 0);
-        if (it < VIT && j0 + r < sq.len) vreg[u][0] = *reinterpret_cast<const uint4*>(vbase + int64_t(j0 + r) * p.ts + c);
-      }
-    }
+    kt.load(kbase, p.ts, j0, sq.len);
+    vt.load(vbase, p.ts, j0, sq.len);
     if (tid < BN) {
       const int j = j0 + tid;
       const bool in = j < sq.len;
@@ -131,33 +110,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   };
 
   auto commit = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int it = tid + u * 256;
-      const int r = it / (D / CH), c = (it % (D / CH)) * CH;
-      if (it < KCH) *reinterpret_cast<uint4*>(&Ks[buf][r * KP + c]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int it = tid + u * 256;
-      if (it >= VIT) continue;
-      if constexpr (PAIR) {
-        const int r = 2 * (it % (BN / 2)), c = (it / (BN / 2)) * CH;
-        const uint32_t aw[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
-        const uint32_t bw[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(&Vt[buf][(c + e) * VP + r]) = lo | (hi << 16);
-        }
-      } else {
-        const int r = it % BN, c = (it / BN) * CH;
-        const float* f = reinterpret_cast<const float*>(&vreg[u][0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) reinterpret_cast<float*>(Vt[buf])[(c + e) * VP + r] = f[e];
-      }
-    }
+    kt.template store<KP>(Ks[buf]);
+    vt.template store<VP>(Vs[buf]);
     if (tid < BN) bj_s[buf][tid] = breg;
     if (tid < NL) lut_s[buf][tid] = lreg;
   };
@@ -199,7 +153,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     for (int t = 0; t < NKT; ++t) {
       f32x16 acc = zero16();
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) acc = TR::mma(TR::ld(&Ks[buf][(32 * t + li) * KP + q * KS + g * E]), Qf[q], acc);
+      for (int q = 0; q < NQ; ++q) acc = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], acc);
       if (cls != TILE_BAND) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) y[t][v] = fmaf(acc[v], p.scale_log2, bj_s[buf][32 * t + acc_row(v, g)]);
@@ -254,15 +208,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       for (int q = 0; q < 32 / KS; ++q) {
         const frag pb = TR::pack(&y[t][q * E]);
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const T* vr = &Vt[buf][(32 * nd + li) * VP + 32 * t];
-          frag va;
-          if constexpr (E == 8)
-            va = TR::ld2x4(vr + 16 * q + 4 * g, vr + 16 * q + 8 + 4 * g);
-          else
-            va = TR::ld(vr + fed_row<E>(q, 0, g));
-          O[nd] = TR::mma(va, pb, O[nd]);
-        }
+        for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pb, O[nd]);
       }
     if (kb + 1 < nkb) commit(buf ^ 1);
     __syncthreads();

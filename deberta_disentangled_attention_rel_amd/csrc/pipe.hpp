@@ -1,0 +1,109 @@
+// Row tiles of a [T,H,D] tensor (one head): register prefetch from global
+// memory, 16-byte stores into a row-major LDS tile, and MFMA fragment reads.
+//
+// Fragments read from a row-major LDS tile X (pitch P elements):
+//  * ld_row: 8 (16-bit) or 1 (fp32) consecutive elements of one row, for an
+//    operand whose lane index is the tile row and whose contraction index
+//    runs along the row;
+//  * ld_col: for an operand whose lane index is the tile COLUMN and whose
+//    contraction index runs down the rows, lane (li, g) needs
+//      X[r0 + 4g + s][c0 + li], X[r0 + 8 + 4g + s][c0 + li], s = 0..3
+//    (16-bit; the register order of a 32x32 accumulator fed back as an
+//    operand) or X[r0 + acc_row(q, g)][c0 + li] (fp32). For 16-bit types this
+//    is two gfx950 transposing LDS reads: within each 16-lane group, lane i
+//    receives element i % 4 of the 8-byte words addressed by lanes
+//    4k + i / 4 (k = 0..3), so pointing source lane s of the group at row
+//    r0 + 4g + s/4, column c0 + 16*(group parity) + 4*(s % 4) hands lane i
+//    rows r0 + 4g + k of column c0 + li.
+#pragma once
+
+#include "common.hpp"
+
+namespace dfa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename TR>
+__device__ __forceinline__ typename TR::frag ld_row(const typename TR::T* X, int P, int row, int col) {
+  return TR::ld(X + row * P + col);
+}
+
+// Column fragment for contraction step q: rows r0 + 16q + {4g..4g+3, 8+4g..8+4g+3}
+// (16-bit, two transposing reads) or row r0 + acc_row(q, g) (fp32), column
+// c0 + (lane % 32).
+template <typename TR>
+__device__ __forceinline__ typename TR::frag ld_col(const typename TR::T* X, int P, int r0, int c0, int q) {
+  using T = typename TR::T;
+  const int lane = threadIdx.x & 63;
+  if constexpr (TR::E == 8) {
+    const int b = lane >> 4, s = lane & 15;
+    const T* a = X + (r0 + 16 * q + 4 * (b >> 1) + (s >> 2)) * P + c0 + 16 * (b & 1) + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * P));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(typename TR::frag, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  } else {
+    return X[(r0 + acc_row(q, lane >> 5)) * P + c0 + (lane & 31)];
+  }
+}
+
+// Pitches (elements) of row-major tiles. 16-bit: +8 keeps rows 16-byte
+// aligned and puts consecutive rows 4 banks apart (conflict-free 16-byte row
+// reads); tiles read only through ld_col use +16 (the four rows of a
+// transposing read land 8 banks apart). fp32: odd pitch.
+template <typename T, int W> struct RowPitch {
+  static constexpr int rows = sizeof(T) == 2 ? W + 8 : W + 1;
+  static constexpr int cols = sizeof(T) == 2 ? W + 16 : W + 1;
+};
+
+// A ROWS x D tile of one head of a [T,H,D] tensor, prefetched into registers
+// by all NT threads (16-byte chunks) and committed to LDS.
+template <typename T, int ROWS, int D, int NT>
+struct RowTile {
+  static constexpr int CH = 16 / int(sizeof(T));
+  static constexpr int NC = D / CH;
+  static constexpr int CHUNKS = ROWS * NC;
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;
+  uint4 r[PER];
+  int row[PER];
+  int col[PER];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int it = threadIdx.x + u * NT;
+      row[u] = it < CHUNKS ? it / NC : ROWS;  // ROWS marks an idle slot
+      col[u] = (it % NC) * CH;
+    }
+  }
+  // rows row0 .. row0+ROWS-1 of `base` (token stride ts); rows >= nvalid -> 0
+  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ts, int row0, int nvalid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      r[u] = make_uint4(0, 0, 0, 0);
+      if (row[u] < ROWS && row0 + row[u] < nvalid)
+        r[u] = *reinterpret_cast<const uint4*>(base + int64_t(row0 + row[u]) * ts + col[u]);
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (row[u] < ROWS) {
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint4*>(lds + row[u] * P + col[u]) = r[u];
+        } else {
+          // odd fp32 pitch: rows are only 4-byte aligned
+          float* d = reinterpret_cast<float*>(lds) + row[u] * P + col[u];
+          const float* s = reinterpret_cast<const float*>(&r[u]);
+          d[0] = s[0];
+          d[1] = s[1];
+          d[2] = s[2];
+          d[3] = s[3];
+        }
+      }
+  }
+};
+
+}  // namespace dfa
