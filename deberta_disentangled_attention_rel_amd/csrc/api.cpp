@@ -110,7 +110,7 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
     o = align_up(o + bytes, kAlign);
     return at;
   };
-  pl.lut = take((2 * (2 * size_t(s->max_seqlen) - 1) + 2) * sizeof(int32_t));
+  pl.lut = take(2 * (2 * size_t(s->max_seqlen) - 1) * sizeof(int32_t));
   pl.c2ps = take(H * T * pl.RP * es);
   pl.p2cs = take(H * T * pl.RP * es);
   pl.ends = take(4 * H * T * es);
@@ -153,6 +153,17 @@ bool narrow_tables(int span, int buckets) {
   return slope <= 1.0 - 1e-9;
 }
 
+// Far field of the tables. For d >= 0, c2p[d] = R-1 and p2c[d] = 0 together
+// hold iff bucket(d) >= att: unbucketed that is d >= span; with log buckets
+// and mid >= 2, mid + ceil(x(d)) >= 2 mid iff x(d) > mid - 1 iff d > span - 1
+// (x(span-1) = mid-1 exactly). By the oddness of bucket, c2p[d] = 0 and
+// p2c[d] = R-1 hold iff d <= -span. With mid = 1 the log part is flat at 1
+// and never reaches att, so there is no far field.
+int far_bound(int span, int buckets, int Lmax) {
+  if (buckets > 0 && buckets / 2 < 2) return Lmax;
+  return span < Lmax ? span : Lmax;
+}
+
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 int check_ptr(const void* ptr, const char* name, size_t al) {
@@ -183,8 +194,9 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
   p.scale_log2 = float(1.4426950408889634 / std::sqrt(3.0 * s->head_dim));
   p.c2p = reinterpret_cast<int32_t*>(ws + pl.lut);
   p.p2c = p.c2p + (2 * size_t(s->max_seqlen) - 1);
-  p.fbounds = p.p2c + (2 * size_t(s->max_seqlen) - 1);
   p.narrow = narrow_tables(span, buckets) ? 1 : 0;
+  p.d_hi = far_bound(span, buckets, s->max_seqlen);
+  p.d_lo = -p.d_hi;
   p.c2ps = ws + pl.c2ps;
   p.p2cs = ws + pl.p2cs;
   p.ends = ws + pl.ends;
@@ -339,8 +351,6 @@ int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                      [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
-      (rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                      [&] { return dfa::launch_lut_bounds(p.Lmax, p.R, p.c2p, p.p2c, p.fbounds, st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
@@ -392,8 +402,6 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                        [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
-        (rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                        [&] { return dfa::launch_lut_bounds(p.Lmax, p.R, p.c2p, p.p2c, p.fbounds, st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||

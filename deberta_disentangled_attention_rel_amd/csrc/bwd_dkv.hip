@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   if (j0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
   const int RP = p.RP;
-  const int d_hi = p.fbounds[0], d_lo = p.fbounds[1];
+  const int d_hi = p.d_hi, d_lo = p.d_lo;
 
   const int jl = wave * 32 + li;  // this lane's key within the block
   const int jw = j0 + jl;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   if (i0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
   const int RP = p.RP;
-  const int d_hi = p.fbounds[0], d_lo = p.fbounds[1];
+  const int d_hi = p.d_hi, d_lo = p.d_lo;
 
   const int il = wave * 32 + li;
   const int iw = i0 + il;  // this lane's query (local index)

@@ -74,48 +74,11 @@ __global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict_
   p2c[n] = p < 0 ? 0 : (p > R - 1 ? R - 1 : p);
 }
 
-// Far-field bounds of the tables. Both tables are monotone (c2p up, p2c
-// down in d), so {d : c2p[d] = R-1 and p2c[d] = 0} is [d_hi, Lmax) and
-// {d : c2p[d] = 0 and p2c[d] = R-1} is (-Lmax, d_lo]. A tile whose d range lies
-// inside one of them sees one C2P row per query and one P2C row per key.
-// out[0] = d_hi (Lmax if empty), out[1] = d_lo (-Lmax if empty). One block,
-// tree reductions in LDS (order-independent min / max).
-__global__ __launch_bounds__(256) void bounds_kernel(int Lmax, int R, const int32_t* __restrict__ c2p,
-                                                     const int32_t* __restrict__ p2c, int32_t* __restrict__ out) {
-  __shared__ int hi_s[256], lo_s[256];
-  const int off = Lmax - 1;
-  int hi = Lmax, lo = -Lmax;
-  for (int d = threadIdx.x; d <= off; d += 256) {
-    if (c2p[off + d] == R - 1 && p2c[off + d] == 0) hi = min(hi, d);
-    if (c2p[off - d] == 0 && p2c[off - d] == R - 1) lo = max(lo, -d);
-  }
-  hi_s[threadIdx.x] = hi;
-  lo_s[threadIdx.x] = lo;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      hi_s[threadIdx.x] = min(hi_s[threadIdx.x], hi_s[threadIdx.x + w]);
-      lo_s[threadIdx.x] = max(lo_s[threadIdx.x], lo_s[threadIdx.x + w]);
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    out[0] = hi_s[0];
-    out[1] = lo_s[0];
-  }
-}
-
 }  // namespace
 
 hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st) {
   const int n = 2 * Lmax - 1;
   lut_kernel<<<(n + 255) / 256, 256, 0, st>>>(Lmax, span, buckets, c2p, p2c);
-  return hipGetLastError();
-}
-
-hipError_t launch_lut_bounds(int Lmax, int R, const int32_t* c2p, const int32_t* p2c, int32_t* out,
-                             hipStream_t st) {
-  bounds_kernel<<<1, 256, 0, st>>>(Lmax, R, c2p, p2c, out);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ struct Params {
   // relative index tables, entry d + Lmax - 1
   int32_t* c2p;
   int32_t* p2c;
-  int32_t* fbounds;         // [2]: d_hi, d_lo of the far field (see launch_lut_bounds)
+  int d_hi, d_lo;           // far field: both tables at their end rows iff d >= d_hi or d <= d_lo
   int narrow;               // 1 if neither table ever steps by more than one row
   // user tensors
   const void *q, *k, *v, *qr, *kr;
@@ -48,8 +48,6 @@ struct Params {
 
 // launchers (each returns hipGetLastError() after its launches)
 hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st);
-hipError_t launch_lut_bounds(int Lmax, int R, const int32_t* c2p, const int32_t* p2c, int32_t* out,
-                             hipStream_t st);
 hipError_t launch_strips(const Params& p, int which, hipStream_t st);  // 0: C2P, 1: P2C
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);

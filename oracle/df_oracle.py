@@ -32,6 +32,7 @@ fused or reordered beyond the definition.
 """
 from __future__ import annotations
 
+import functools
 import math
 from typing import Optional
 
@@ -81,11 +82,19 @@ def bucket_exact(d: int, span: int, buckets: int) -> int:
     return int(math.copysign(mid + k, d))
 
 
+@functools.lru_cache(maxsize=16)
+def _bucket_range(lim: int, span: int, buckets: int) -> np.ndarray:
+    """``bucket(d)`` for d in [-lim, lim] (cached; index d + lim)."""
+    return np.array([bucket_exact(x, span, buckets) for x in range(-lim, lim + 1)],
+                    dtype=np.int64)
+
+
 def _delta_table(lo: int, hi: int, span: int, buckets: int) -> np.ndarray:
     """``clamp(bucket(d) + att, 0, R - 1)`` for every integer d in [lo, hi]."""
     att, R = att_and_rows(span, buckets)
-    b = np.array([bucket_exact(x, span, buckets) for x in range(lo, hi + 1)],
-                 dtype=np.int64)
+    lim = max(abs(lo), abs(hi))
+    lim = 1 << max(4, (lim - 1).bit_length())  # a few cached sizes cover every call
+    b = _bucket_range(lim, span, buckets)[lo + lim: hi + lim + 1]
     return np.clip(b + att, 0, R - 1)
 
 
@@ -171,11 +180,13 @@ def _probs(S: np.ndarray, valid: np.ndarray) -> tuple:
 # forward
 
 def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
-            cu_seqlens=None, batch=None, seqlen=None, return_probs: bool = False):
+            cu_seqlens=None, batch=None, seqlen=None, return_probs: bool = False,
+            heads=None):
     """Output ``[T, H, D]`` and LSE ``[H, T]`` (natural log), float64.
 
     ``q, k, v`` are ``[T, H, D]``; ``q_r, k_r`` are ``[H, R, D]``.
-    With ``return_probs`` also returns ``{(seq, head): P}``.
+    ``heads`` restricts the work to a subset of heads (other heads are left
+    0 / -inf). With ``return_probs`` also returns ``{(seq, head): P}``.
     """
     q, k, v, q_r, k_r = (np.asarray(x, dtype=np.float64) for x in (q, k, v, q_r, k_r))
     T, H, D = q.shape
@@ -184,9 +195,10 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
     out = np.zeros((T, H, D))
     lse = np.full((H, T), -np.inf)
     probs = {}
+    hs = range(H) if heads is None else heads
     for n, (st, en) in enumerate(sequences(T, cu_seqlens, batch, seqlen)):
         valid = _valid(key_mask, st, en)
-        for h in range(H):
+        for h in hs:
             S = scores(q[st:en, h], k[st:en, h], q_r[h], k_r[h], span, buckets)
             P, l = _probs(S, valid)
             out[st:en, h] = P @ v[st:en, h]

@@ -1,0 +1,177 @@
+"""CPU tests of the C ABI (no GPU needed, no kernel launched).
+
+* the library loads and exports every function declared in include/df_attn.h;
+* every invalid argument is rejected on the host with the documented code
+  before anything touches a device (fake, never-dereferenced pointers);
+* the two properties of the relative-index tables that the kernels rely on
+  hold for the oracle's tables: the far-field bound (both tables at their end
+  rows exactly when |d| >= span) and the no-skip criterion for log buckets.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "df_attn.h")
+
+
+@pytest.fixture(scope="module")
+def df():
+    import deberta_disentangled_attention_rel_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from deberta_disentangled_attention_rel_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(df_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(df):
+    names = header_functions()
+    assert "df_attn_fwd" in names and "df_attn_bwd" in names
+    lib = ctypes.CDLL(df.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(df.EXPORTED)
+    assert lib.df_attn_version() >= 100
+
+
+def _shape(df, **kw):
+    d = dict(batch=2, max_seqlen=128, total_tokens=256, num_heads=4, head_dim=64, dtype=0,
+             tok_stride=256, head_stride=64)
+    d.update(kw)
+    return df.Shape(**d)
+
+
+@pytest.mark.parametrize("kw,span,buckets,code", [
+    (dict(), 512, 256, 0),
+    (dict(), 32, 0, 0),
+    (dict(head_dim=48), 512, 256, 2),
+    (dict(head_dim=256), 512, 256, 2),
+    (dict(dtype=3), 512, 256, 2),
+    (dict(batch=0), 512, 256, 1),
+    (dict(max_seqlen=0), 512, 256, 1),
+    (dict(num_heads=0), 512, 256, 1),
+    (dict(total_tokens=-1), 512, 256, 1),
+    (dict(tok_stride=252), 512, 256, 1),          # not a multiple of 8
+    (dict(head_stride=32), 512, 256, 1),          # rows overlap
+    (dict(tok_stride=128), 512, 256, 1),          # heads overlap the next token
+    (dict(), 0, 0, 1),                             # span must be >= 1
+    (dict(), 512, 1, 1),                           # buckets must be 0 or >= 2
+    (dict(), 100, 256, 1),                         # span - 1 <= buckets / 2
+    (dict(), 512, -2, 1),
+])
+def test_supported_codes(df, kw, span, buckets, code):
+    assert df.supported(_shape(df, **kw), span, buckets) == code
+
+
+def test_workspace_sizes(df):
+    s = _shape(df)
+    w0, w1 = df.workspace_size(0, s, 512, 256), df.workspace_size(1, s, 512, 256)
+    assert 0 < w0 < w1
+    # forward: two tables + two strips [H][T][R] + four end columns, 256-byte aligned pieces
+    T, H, R, L = 256, 4, 512, 128
+    expect = [2 * (2 * L - 1) * 4, H * T * R * 2, H * T * R * 2, 4 * H * T * 2]
+    assert w0 == sum((x + 255) // 256 * 256 for x in expect)
+    assert df.workspace_size(2, s, 512, 256) == 0
+    assert df.workspace_size(0, _shape(df, head_dim=48), 512, 256) == 0
+
+
+FAKE = 1 << 20  # 256-byte aligned, never dereferenced
+
+
+def _fwd(df, shape, ptrs, ws_bytes=1 << 40, span=512, buckets=256, cu=None):
+    L = df.lib()
+    vp = [ctypes.c_void_p(x) if x else None for x in ptrs]
+    return L.df_attn_fwd(ctypes.byref(shape), vp[0], vp[1], vp[2], vp[3], vp[4], span, buckets,
+                         None, cu, vp[5], vp[6], ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def test_fwd_rejects_on_host(df):
+    L = df.lib()
+    s = _shape(df)
+    ok = [FAKE] * 7
+    for k in range(7):
+        bad = list(ok)
+        bad[k] = 0
+        assert _fwd(df, s, bad) == 1
+        assert "NULL" in L.df_last_error().decode()
+    mis = list(ok)
+    mis[0] = FAKE + 2                         # q misaligned
+    assert _fwd(df, s, mis) == 1
+    assert _fwd(df, s, ok, ws_bytes=1024) == 3
+    assert "workspace" in L.df_last_error().decode()
+    assert _fwd(df, _shape(df, total_tokens=200), ok) == 1   # padded T mismatch
+    assert _fwd(df, _shape(df, head_dim=32, dtype=2), ok, span=0) == 1
+    assert L.df_strerror(3).decode() == "workspace too small"
+
+
+def test_bwd_and_index_reject_on_host(df):
+    L = df.lib()
+    s = _shape(df)
+    p = [ctypes.c_void_p(FAKE)] * 15
+    rc = L.df_attn_bwd(ctypes.byref(s), *p[:5], 512, 256, None, None, *p[5:8],
+                       *p[8:13], ctypes.c_void_p(FAKE), 16, None)
+    assert rc == 3
+    rc = L.df_attn_bwd(ctypes.byref(s), *p[:5], 512, 256, None, None, *p[5:7], None,
+                       *p[8:13], ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert rc == 1 and "dout" in L.df_last_error().decode()
+    assert L.df_build_rel_index(0, 512, 256, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == 1
+    assert L.df_build_rel_index(64, 512, 256, None, ctypes.c_void_p(FAKE), None) == 1
+    assert L.df_build_rel_index(64, 100, 256, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == 1
+
+
+def test_profile_api_without_enable(df):
+    L = df.lib()
+    ms = (ctypes.c_float * 9)()
+    n = (ctypes.c_int * 9)()
+    assert L.df_attn_profile_read(ms, n, 9) == 1
+    assert L.df_attn_stage_name(4).decode() == "bwd_dkv"
+    assert L.df_attn_stage_name(99).decode() == ""
+
+
+# ----------------------------------------------------------------------------
+# table properties the kernels rely on
+
+CONFIGS = [(512, 256), (512, 0), (32, 0), (12, 8), (81, 10), (300, 256), (6, 4), (40, 16),
+           (1, 0), (4, 2), (5, 3), (200, 64), (64, 32)]
+
+
+@pytest.mark.parametrize("span,buckets", CONFIGS)
+def test_far_field_bound(span, buckets):
+    # both tables at their end rows exactly when |d| >= span (no far field when mid = 1)
+    L = 700
+    c2p, p2c = oracle.rel_luts(L, span, buckets)
+    att, R = oracle.att_and_rows(span, buckets)
+    d = np.arange(-(L - 1), L)
+    left = (c2p == R - 1) & (p2c == 0)
+    right = (c2p == 0) & (p2c == R - 1)
+    if buckets > 0 and buckets // 2 < 2:
+        assert not left.any() and not right.any()
+        return
+    assert np.array_equal(left, d >= span)
+    assert np.array_equal(right, d <= -span)
+
+
+@pytest.mark.parametrize("span,buckets", CONFIGS + [(260, 256), (200, 256), (131, 256), (400, 200)])
+def test_narrow_criterion(span, buckets):
+    # (mid-1) <= mid ln((span-1)/mid) implies no table ever steps by more than one row
+    c2p, p2c = oracle.rel_luts(1500, span, buckets)
+    steps = max(np.abs(np.diff(c2p)).max(), np.abs(np.diff(p2c)).max())
+    mid = buckets // 2
+    narrow = buckets == 0 or mid <= 1 or (mid - 1) / (mid * math.log((span - 1) / mid)) <= 1 - 1e-9
+    if narrow:
+        assert steps <= 1
+    if buckets == 256 and span in (260, 200, 131):
+        assert not narrow and steps > 1   # these really skip rows
