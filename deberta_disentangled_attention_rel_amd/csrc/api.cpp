@@ -194,7 +194,9 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
   p.scale_log2 = float(1.4426950408889634 / std::sqrt(3.0 * s->head_dim));
   p.c2p = reinterpret_cast<int32_t*>(ws + pl.lut);
   p.p2c = p.c2p + (2 * size_t(s->max_seqlen) - 1);
-  p.narrow = narrow_tables(span, buckets) ? 1 : 0;
+  // narrow kernels keep both rows of a table entry as 16-bit byte offsets
+  const size_t esize = s->dtype == DF_FP32 ? 4 : 2;
+  p.narrow = (narrow_tables(span, buckets) && size_t(R - 1) * esize <= 0xffff) ? 1 : 0;
   p.d_hi = far_bound(span, buckets, s->max_seqlen);
   p.d_lo = -p.d_hi;
   p.c2ps = ws + pl.c2ps;
@@ -351,8 +353,7 @@ int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                      [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
-      (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
-      (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
+      (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
     return rc;
   return ok();
@@ -402,8 +403,7 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                        [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
-        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 0, st); })) ||
-        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, 1, st); })) ||
+        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
         (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||
         (rc = run_stage(DF_STAGE_DQ, st, "dq kernel", [&] { return dfa::launch_bwd_dq(p, st); })) ||

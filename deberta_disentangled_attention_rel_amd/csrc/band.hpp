@@ -6,8 +6,10 @@
 //    the C2P term is one value per query and the P2C term one value per key;
 //  * far-right (dhi <= d_lo): C2P row 0 and P2C row R-1, likewise;
 //  * band: anything else. The pair's rows come from the index tables (a
-//    slice of BM+BN-1 entries, packed c2p | p2c << 16, staged in LDS) and
-//    the values from LDS windows of the strips:
+//    slice of BM+BN-1 entries, packed c2p | p2c << 16, staged in LDS; the
+//    narrow kernels store them as byte offsets) and the values from LDS
+//    windows of the strips (a kernel may instead read the term whose row is
+//    shared by the lanes of a half straight from the strip):
 //      C2P window, one row per query il: strip columns [cs_il, cs_il + BN + 8)
 //        with cs_il = c2p[i0+il - (j0+BN-1)] rounded down to 8 (the smallest
 //        row the query meets in this tile);
@@ -44,6 +46,19 @@ __device__ __forceinline__ uint32_t lut_entry(const Params& p, int d) {
 
 __device__ __forceinline__ int lut_c(uint32_t e) { return int(e & 0xffffu); }
 __device__ __forceinline__ int lut_p(uint32_t e) { return int(e >> 16); }
+
+// The same entry with both rows scaled to byte offsets into rows of ES-byte
+// elements (narrow kernels: the window gathers then need one add each).
+template <int ES>
+__device__ __forceinline__ uint32_t lut_entry_bytes(const Params& p, int d) {
+  const uint32_t e = lut_entry(p, d);
+  return (e & 0xffffu) * ES | ((e >> 16) * ES) << 16;
+}
+// Byte offset of the 8-element-aligned window start below a scaled row.
+template <int ES>
+__device__ __forceinline__ int win_start_bytes(int row_bytes) {
+  return row_bytes & ~(8 * ES - 1);
+}
 
 // Row pitches (elements) of the strip windows: an odd number of dwords for
 // 16-bit types (odd number of floats for fp32), so that lanes reading

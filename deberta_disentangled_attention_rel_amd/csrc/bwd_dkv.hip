@@ -18,6 +18,11 @@
 // The strip row of key j is written by an ordered walk over the queries (one
 // step per tile in the far field). dK here is the dS^T Q part; the dP2C Q_r
 // term is added by the relative-gradient GEMM.
+//
+// Band tiles gather both relative terms from LDS strip windows (one C2P row
+// per query, one P2C row per key); the table slice holds byte offsets, so a
+// gather address is one add, and the two values and the per-query term are
+// joined with one packed dot product.
 #include "band.hpp"
 #include "pipe.hpp"
 #include "walk.hpp"
@@ -31,7 +36,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
+  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32, ES = int(sizeof(T));
   constexpr int BN = 128, BM = 32 * NQT, NL = BM + BN - 1;
   constexpr int QP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;   // C2P window: one row per query
@@ -46,13 +51,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
   __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
-  __shared__ int cs_s[NARROW ? BM : 1];
+  __shared__ int cb_s[NARROW ? BM : 1];  // per query: byte base of its C2P window row
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
-  const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
-  const int h = blockIdx.y;
-  const int j0 = blockIdx.x * BN;
+  const AttnBlock blk = attn_block((p.Lmax + 127) / 128, p.H);
+  const SeqRange sq = seq_range(p.cu, blk.z, p.Lmax);
+  const int h = blk.h;
+  const int j0 = blk.x * BN;
   if (j0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
   const int RP = p.RP;
@@ -112,7 +118,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       ureg = ok ? a - lse[ic] * kLog2e : -INFINITY;
       dreg = ok ? dlt[ic] : 0.f;
     }
-    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+    if (cls == TILE_BAND && tid < NL)
+      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
   auto commit = [&](int buf) {
     qt.template store<QP>(Qs[buf]);
@@ -147,10 +154,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if constexpr (NARROW) {
       if (cls == TILE_BAND) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
+                                      [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
         stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
-        if (tid < BM) cs_s[tid] = lut_c(lut_s[buf][tid]) & ~7;
+                                       [&](int r) { return win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - r])) / ES; });
+        if (tid < BM) cb_s[tid] = tid * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][tid]));
         __syncthreads();
       }
     }
@@ -158,7 +165,9 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     float bj = kbias;
     if (cls == TILE_FAR_LEFT) bj = b_end0;
     if (cls == TILE_FAR_RIGHT) bj = b_end1;
-    const int ps = NARROW ? (lut_p(lut_s[buf][NL - 1 - jl]) & ~7) : 0;
+    // byte base of this key's P2C window row
+    const char* wp = reinterpret_cast<const char*>(Wp) + jl * WPP * ES -
+                     (NARROW && cls == TILE_BAND ? win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - jl])) : 0);
 
     float colsum = 0.f;
 #pragma unroll
@@ -177,11 +186,12 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         if (cls == TILE_BAND) {
           const uint32_t e = lut_s[buf][il - jl + BN - 1];
           if constexpr (NARROW) {
-            rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs_s[il]]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps]);
+            rel = TR::add2(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(Wc) + cb_s[il] + lut_c(e)),
+                           *reinterpret_cast<const T*>(wp + lut_p(e)), rel);
           } else {
             const int ii = min(i0 + il, sq.len - 1);
-            rel += TR::to_f(c2pstrip[int64_t(ii) * RP + lut_c(e)]) +
-                   TR::to_f(p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)]);
+            rel = TR::add2(c2pstrip[int64_t(ii) * RP + lut_c(e)], p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)],
+                           rel);
           }
         }
         P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel) + bj);
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
             const int il = 32 * u + k;
             if (i0 + il >= sq.len) break;
             const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lut_p(lut_s[buf][il - jl + BN - 1]), val);
+            walk.step(lut_p(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), val);
           }
         }
       }
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 
 template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
-  dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
+  dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NQT = (DT == DF_FP32_T) ? 1 : 2;
   dkv_kernel<DT, D, NQT, NARROW><<<grid, 256, 0, st>>>(p);
 }

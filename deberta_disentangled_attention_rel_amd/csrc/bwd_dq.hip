@@ -17,6 +17,10 @@
 // step per tile in the far field, where the whole tile shares one row). dQ
 // here is the dS K part; the dC2P K_r term is added by the relative-gradient
 // GEMM. No atomics.
+//
+// Band tiles recompute the relative terms as the forward does: C2P from the
+// query's LDS strip window, P2C straight from the strip in L2, both issued
+// ahead of the score MFMAs. The tile body is compiled once per tile class.
 #include "band.hpp"
 #include "pipe.hpp"
 #include "walk.hpp"
@@ -30,11 +34,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
+  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32, ES = int(sizeof(T));
   constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
   constexpr int KP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
-  constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
   static_assert(NL <= 256, "one table entry per thread");
   using KTile = RowTile<T, BN, D, 256>;
 
@@ -43,14 +46,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   __shared__ __align__(16) float bj_s[2][BN];
   __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
-  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
-  __shared__ int ps_s[NARROW ? BN : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
-  const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
-  const int h = blockIdx.y;
-  const int i0 = blockIdx.x * BM;
+  const AttnBlock blk = attn_block((p.Lmax + 127) / 128, p.H);
+  const SeqRange sq = seq_range(p.cu, blk.z, p.Lmax);
+  const int h = blk.h;
+  const int i0 = blk.x * BM;
   if (i0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
   const int R = p.R, RP = p.RP;
@@ -109,7 +111,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
       if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
       breg = ok ? b : -INFINITY;
     }
-    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+    if (cls == TILE_BAND && tid < NL)
+      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
 
   auto commit = [&](int buf) {
@@ -136,78 +139,108 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
     if (kb + 1 < nkb) prefetch(kb + 1);
-    if constexpr (NARROW) {
-      if (cls == TILE_BAND) {
+
+    // the tile body, compiled once per tile class as straight-line code
+    auto body = [&](auto band_c) {
+      constexpr bool BAND = decltype(band_c)::value;
+      if constexpr (BAND && NARROW) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
-        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
-        if (tid < BN) ps_s[tid] = lut_p(lut_s[buf][NL - 1 - tid]) & ~7;
+                                      [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
         __syncthreads();
       }
-    }
+      const float w = (BAND ? 0.f : (cls == TILE_FAR_LEFT ? a_end1 : a_end0)) - lse2;
 
-    float a = 0.f;
-    if (cls == TILE_FAR_LEFT) a = a_end1;
-    if (cls == TILE_FAR_RIGHT) a = a_end0;
-    const float w = a - lse2;
-    const int cs = NARROW ? (lut_c(lut_s[buf][il]) & ~7) : 0;
-
-    float rowsum = 0.f;
+      // relative terms (log2 domain) of this lane's keys; band tiles gather
+      // them before the score MFMAs so the gather latency overlaps them
+      float rel[NKT][16];
+      if constexpr (BAND) {
+        const uint32_t* lrow = &lut_s[buf][il + BN - 1];  // entry of key jl: lrow[-jl]
+        if constexpr (NARROW) {
+          // C2P from this row's LDS window; P2C straight from the strip in L2
+          // (for a fixed key the lanes of a half read one contiguous run)
+          const char* wc = reinterpret_cast<const char*>(Wc) + il * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
+          const BufView prow = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
+          const int soff = j0 * RP * ES;
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-      f32x16 S = zero16(), dP = zero16();
+          for (int t = 0; t < NKT; ++t)
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        S = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], S);
-        dP = TR::mma(ld_row<TR>(Vs[buf], KP, 32 * t + li, q * KS + g * E), dOf[q], dP);
-      }
-      float dS[16];
+            for (int v = 0; v < 16; ++v) {
+              const int jl = 32 * t + acc_row(v, g);
+              const uint32_t e = lrow[-jl];
+              rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
+                                   buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
+            }
+        } else {
+          const T* crow = c2pstrip + int64_t(qin ? iw : sq.len - 1) * RP;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int jl = 32 * t + acc_row(v, g);
-        float rel = bj_s[buf][jl];
-        if (cls == TILE_BAND) {
-          const uint32_t e = lut_s[buf][il - jl + BN - 1];
-          if constexpr (NARROW) {
-            rel += TR::to_f(Wc[il * WCP + lut_c(e) - cs]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps_s[jl]]);
-          } else {
-            const int jj = min(j0 + jl, sq.len - 1);
-            rel += TR::to_f(c2pstrip[int64_t(qin ? iw : sq.len - 1) * RP + lut_c(e)]) +
-                   TR::to_f(p2cstrip[int64_t(jj) * RP + lut_p(e)]);
-          }
+          for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int jl = 32 * t + acc_row(v, g);
+              const uint32_t e = lrow[-jl];
+              const int jj = min(j0 + jl, sq.len - 1);
+              rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
+            }
         }
-        const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel) + w);
-        dS[v] = P * (dP[v] - dlt);
-      }
-#pragma unroll
-      for (int q = 0; q < 32 / KS; ++q) {
-        const frag sb = TR::pack(&dS[q * E]);
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) dQt[nd] = TR::mma(ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q), sb, dQt[nd]);
-      }
-      // dC2P: ordered walk over this subtile's keys
-      if (cls != TILE_BAND) {
-        float rs = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) rs += dS[v];
-        rowsum += rs + xor32(rs);
       } else {
-        float other[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) other[v] = xor32(dS[v]);
-        if (walker) {
+        for (int t = 0; t < NKT; ++t)
 #pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const int jl = 32 * t + k;
-            if (j0 + jl >= sq.len) break;
-            const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lut_c(lut_s[buf][il - jl + BN - 1]), val);
+          for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][32 * t + acc_row(v, g)];
+      }
+
+      float rowsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t) {
+        f32x16 S = zero16(), dP = zero16();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          S = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], S);
+          dP = TR::mma(ld_row<TR>(Vs[buf], KP, 32 * t + li, q * KS + g * E), dOf[q], dP);
+        }
+        float dS[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
+          dS[v] = P * (dP[v] - dlt);
+        }
+#pragma unroll
+        for (int q = 0; q < 32 / KS; ++q) {
+          const frag sb = TR::pack(&dS[q * E]);
+#pragma unroll
+          for (int nd = 0; nd < ND; ++nd)
+            dQt[nd] = TR::mma(ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q), sb, dQt[nd]);
+        }
+        if constexpr (!BAND) {
+          // far tiles: one row, one sum per tile
+          float rs = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) rs += dS[v];
+          rowsum += rs + xor32(rs);
+        } else {
+          // dC2P: ordered walk over this subtile's keys
+          float other[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) other[v] = xor32(dS[v]);
+          if (walker) {
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+              if (j0 + 32 * t + k >= sq.len) break;
+              const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
+              walk.step(lut_c(lut_s[buf][il - 32 * t - k + BN - 1]) / (NARROW ? ES : 1), val);
+            }
           }
         }
       }
-    }
-    if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+      if constexpr (!BAND) {
+        if (walker) walk.step(cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+      }
+    };
+    if (cls == TILE_BAND)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
+
     if (kb + 1 < nkb) commit(buf ^ 1);
     __syncthreads();
   }
@@ -223,7 +256,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 
 template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
-  dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
+  dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
   dq_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
 }

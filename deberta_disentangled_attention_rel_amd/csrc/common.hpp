@@ -51,6 +51,13 @@ template <> struct Tr<DF_BF16_T> {
     return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
   }
   static __device__ __forceinline__ frag zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+  // a + b + c for two stored values (one packed dot product with (1, 1))
+  static __device__ __forceinline__ float add2(T a, T b, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
+  }
 };
 
 template <> struct Tr<DF_FP16_T> {
@@ -76,6 +83,12 @@ template <> struct Tr<DF_FP16_T> {
     return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
   }
   static __device__ __forceinline__ frag zero() { return __builtin_bit_cast(frag, make_uint4(0, 0, 0, 0)); }
+  static __device__ __forceinline__ float add2(T a, T b, float c) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
+  }
 };
 
 template <> struct Tr<DF_FP32_T> {
@@ -91,6 +104,7 @@ template <> struct Tr<DF_FP32_T> {
   static __device__ __forceinline__ frag ld(const T* p) { return *p; }
   static __device__ __forceinline__ frag ld2x4(const T* p0, const T*) { return *p0; }
   static __device__ __forceinline__ frag zero() { return 0.f; }
+  static __device__ __forceinline__ float add2(T a, T b, float c) { return (a + b) + c; }
 };
 
 // ---------------------------------------------------------------------------
@@ -120,6 +134,47 @@ __device__ __forceinline__ float xor32(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer view of `bytes` bytes at `base`: loads at offsets past the end
+// return zero (the hardware range check), so a gather may run past the end
+// of a sequence without touching memory there.
+struct BufView {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ BufView buf_view(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: 32-bit raw data, no swizzle (gfx9 family)
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000)};
+}
+template <typename T>
+__device__ __forceinline__ T buf_load(BufView b, int voff, int soff) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(b.r, voff, soff, 0));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(b.r, voff, soff, 0));
+}
+
+// Compile-time flag passed to a generic lambda, so that a loop body can be
+// instantiated once per tile class (band / far) as straight-line code.
+template <bool B> struct BoolC {
+  static constexpr bool value = B;
+};
+
+// Work-group placement over the 8 XCDs of the chip, each with its own L2.
+// The dispatcher hands consecutive work-group ids to the XCDs in turn;
+// attn_block() renumbers a 1-D grid of nx * H * nseq groups so that every XCD
+// runs one contiguous range of logical blocks (row block fastest, then head,
+// then sequence): the row blocks of one (sequence, head) run together on one
+// XCD and share that head's streamed operands in its L2.
+constexpr int kXcds = 8;
+struct AttnBlock {
+  int x, h, z;
+};
+__device__ __forceinline__ AttnBlock attn_block(int nx, int H) {
+  const int nb = gridDim.x, id = blockIdx.x;
+  const int q = nb / kXcds, r = nb % kXcds, xcd = id % kXcds, slot = id / kXcds;
+  const int logical = xcd * q + (xcd < r ? xcd : r) + slot;
+  return {logical % nx, (logical / nx) % H, logical / (nx * H)};
+}
 
 // Sequence bounds of blockIdx.z: padded (cu == nullptr) or packed.
 struct SeqRange {

@@ -19,8 +19,15 @@
 // Scores are in the log2 domain: y = s*log2(e)*QK + (relative terms). In a
 // far-field tile the per-key P2C value is added in the same FMA and the
 // per-query C2P value a is folded into the row max (exp2(y - (m - a))). A
-// band tile stages the strip windows it needs in LDS and gathers both terms
-// per pair from there (or from global memory when the tables can skip rows).
+// band tile stages each query's C2P strip window in LDS (the lanes gather
+// from different rows) and reads the P2C terms straight from the strip,
+// which stays in L2 (for a fixed key the 32 lanes of a half read one
+// contiguous run of its row). Both gathers are issued ahead of the score
+// MFMAs and joined with one packed dot product. When the tables can skip
+// rows, both terms come from global memory.
+//
+// The tile body is compiled once per tile class (band / far), so each class
+// runs as straight-line code that the scheduler can interleave.
 #include "band.hpp"
 #include "pipe.hpp"
 
@@ -33,11 +40,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32;
+  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32, ES = int(sizeof(T));
   constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
   constexpr int KP = RowPitch<T, D>::rows, VP = RowPitch<T, D>::cols;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
-  constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;
   static_assert(NL <= 256, "one table entry per thread");
   using KTile = RowTile<T, BN, D, 256>;
 
@@ -46,14 +52,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   __shared__ __align__(16) float bj_s[2][BN];
   __shared__ uint32_t lut_s[2][NL];
   __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
-  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
-  __shared__ int ps_s[NARROW ? BN : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
-  const SeqRange sq = seq_range(p.cu, blockIdx.z, p.Lmax);
-  const int h = blockIdx.y;
-  const int i0 = blockIdx.x * BM;
+  const AttnBlock blk = attn_block((p.Lmax + 127) / 128, p.H);
+  const SeqRange sq = seq_range(p.cu, blk.z, p.Lmax);
+  const int h = blk.h;
+  const int i0 = blk.x * BM;
   if (i0 >= sq.len) return;
   const int64_t T_ = p.T, HT = int64_t(p.H) * p.T;
   const int RP = p.RP;
@@ -106,7 +111,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
       breg = ok ? b : -INFINITY;
     }
-    if (cls == TILE_BAND && tid < NL) lreg = lut_entry(p, i0 - j0 - BN + 1 + tid);
+    if (cls == TILE_BAND && tid < NL)
+      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
 
   auto commit = [&](int buf) {
@@ -132,84 +138,107 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     const int cls = cls_of(kb);
     if (kb + 1 < nkb) prefetch(kb + 1);
 
-    if constexpr (NARROW) {
-      if (cls == TILE_BAND) {
+    // the tile body, compiled once per tile class as straight-line code
+    auto body = [&](auto band_c) {
+      constexpr bool BAND = decltype(band_c)::value;
+      if constexpr (BAND && NARROW) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return lut_c(lut_s[buf][r]) & ~7; });
-        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return lut_p(lut_s[buf][NL - 1 - r]) & ~7; });
-        if (tid < BN) ps_s[tid] = lut_p(lut_s[buf][NL - 1 - tid]) & ~7;
+                                      [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
         __syncthreads();
       }
-    }
+      const float a = BAND ? 0.f : (cls == TILE_FAR_LEFT ? a_end1 : a_end0);
 
-    float a = 0.f;
-    if (cls == TILE_FAR_LEFT) a = a_end1;
-    if (cls == TILE_FAR_RIGHT) a = a_end0;
-    const int cs = NARROW ? (lut_c(lut_s[buf][il]) & ~7) : 0;
-
-    float y[NKT][16];
+      // relative terms (log2 domain) of this lane's 16*NKT keys. Band tiles
+      // gather them before the score MFMAs so the LDS latency overlaps them.
+      float rel[NKT][16];
+      if constexpr (BAND) {
+        const uint32_t* lrow = &lut_s[buf][il + BN - 1];  // entry of key jl: lrow[-jl]
+        if constexpr (NARROW) {
+          // C2P from this row's LDS window; P2C straight from the strip in
+          // L2 (for a fixed key the 32 lanes of a half read one contiguous
+          // run of its strip row; keys past the sequence end read zero)
+          const char* wc = reinterpret_cast<const char*>(Wc) + il * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
+          const BufView prow = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
+          const int soff = j0 * RP * ES;
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
-      f32x16 acc = zero16();
+          for (int t = 0; t < NKT; ++t)
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) acc = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], acc);
-      if (cls != TILE_BAND) {
+            for (int v = 0; v < 16; ++v) {
+              const int jl = 32 * t + acc_row(v, g);
+              const uint32_t e = lrow[-jl];
+              rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
+                                   buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
+            }
+        } else {
+          const T* crow = c2pstrip + int64_t(qin ? iw : sq.len - 1) * RP;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) y[t][v] = fmaf(acc[v], p.scale_log2, bj_s[buf][32 * t + acc_row(v, g)]);
+          for (int t = 0; t < NKT; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int jl = 32 * t + acc_row(v, g);
+              const uint32_t e = lrow[-jl];
+              const int jj = min(j0 + jl, sq.len - 1);
+              rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
+            }
+        }
       } else {
 #pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][32 * t + acc_row(v, g)];
+      }
+
+      float y[NKT][16];
+#pragma unroll
+      for (int t = 0; t < NKT; ++t) {
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], acc);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) y[t][v] = fmaf(acc[v], p.scale_log2, rel[t][v]);
+      }
+      // online softmax (log2 domain); a is this tile's per-row C2P value
+      float mt = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, y[t][v]);
+      mt = fmaxf(mt, xor32(mt)) + a;
+      const float mnew = fmaxf(m, mt);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = fast_exp2(m - msafe);
+      const float shift = msafe - a;
+      float ls = 0.f;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int jl = 32 * t + acc_row(v, g);
-          const uint32_t e = lut_s[buf][il - jl + BN - 1];
-          float rel;
-          if constexpr (NARROW) {
-            rel = TR::to_f(Wc[il * WCP + lut_c(e) - cs]) + TR::to_f(Wp[jl * WPP + lut_p(e) - ps_s[jl]]);
-          } else {
-            const int jj = min(j0 + jl, sq.len - 1);
-            rel = TR::to_f(c2pstrip[int64_t(qin ? iw : sq.len - 1) * RP + lut_c(e)]) +
-                  TR::to_f(p2cstrip[int64_t(jj) * RP + lut_p(e)]);
-          }
-          y[t][v] = fmaf(acc[v], p.scale_log2, rel + bj_s[buf][jl]);
+          y[t][v] = fast_exp2(y[t][v] - shift);
+          ls += y[t][v];
         }
+      l = l * alpha + ls;
+      m = mnew;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
       }
-    }
-    // online softmax (log2 domain); a is this tile's per-row C2P value
-    float mt = -INFINITY;
+      // O^T += V^T P^T
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
+      for (int t = 0; t < NKT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, y[t][v]);
-    mt = fmaxf(mt, xor32(mt)) + a;
-    const float mnew = fmaxf(m, mt);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - msafe);
-    const float shift = msafe - a;
-    float ls = 0.f;
+        for (int q = 0; q < 32 / KS; ++q) {
+          const frag pb = TR::pack(&y[t][q * E]);
 #pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        y[t][v] = fast_exp2(y[t][v] - shift);
-        ls += y[t][v];
-      }
-    l = l * alpha + ls;
-    m = mnew;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int t = 0; t < NKT; ++t)
-#pragma unroll
-      for (int q = 0; q < 32 / KS; ++q) {
-        const frag pb = TR::pack(&y[t][q * E]);
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pb, O[nd]);
-      }
+          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pb, O[nd]);
+        }
+    };
+    if (cls == TILE_BAND)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
+
     if (kb + 1 < nkb) commit(buf ^ 1);
     __syncthreads();
   }
@@ -228,7 +257,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
 
 template <int DT, int D, bool NARROW>
 void launch_fwd_d(const Params& p, hipStream_t st) {
-  dim3 grid(unsigned((p.Lmax + 127) / 128), unsigned(p.H), unsigned(p.nseq));
+  dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
   fwd_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
 }

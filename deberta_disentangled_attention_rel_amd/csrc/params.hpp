@@ -48,7 +48,7 @@ struct Params {
 
 // launchers (each returns hipGetLastError() after its launches)
 hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st);
-hipError_t launch_strips(const Params& p, int which, hipStream_t st);  // 0: C2P, 1: P2C
+hipError_t launch_strips(const Params& p, hipStream_t st);  // both strips
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkv(const Params& p, hipStream_t st);

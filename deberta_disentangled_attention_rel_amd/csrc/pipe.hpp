@@ -48,6 +48,19 @@ __device__ __forceinline__ typename TR::frag ld_col(const typename TR::T* X, int
   }
 }
 
+// Row fragment in the same contraction order as ld_col / a fed-back
+// accumulator: columns col0 + 16q + {4g..4g+3, 8+4g..8+4g+3} (16-bit) or
+// col0 + acc_row(q, g) (fp32) of one row. Pair it with ld_col operands.
+template <typename TR>
+__device__ __forceinline__ typename TR::frag ld_row_fed(const typename TR::T* X, int P, int row, int col0, int q) {
+  const int g = (threadIdx.x & 63) >> 5;
+  const typename TR::T* r = X + row * P + col0;
+  if constexpr (TR::E == 8)
+    return TR::ld2x4(r + 16 * q + 4 * g, r + 16 * q + 8 + 4 * g);
+  else
+    return r[acc_row(q, g)];
+}
+
 // Pitches (elements) of row-major tiles. 16-bit: +8 keeps rows 16-byte
 // aligned and puts consecutive rows 4 banks apart (conflict-free 16-byte row
 // reads); tiles read only through ld_col use +16 (the four rows of a
@@ -58,7 +71,7 @@ template <typename T, int W> struct RowPitch {
 };
 
 // A ROWS x D tile of one head of a [T,H,D] tensor, prefetched into registers
-// by all NT threads (16-byte chunks) and committed to LDS.
+// by all NT threads (16-byte chunks) and committed to a row-major LDS tile.
 template <typename T, int ROWS, int D, int NT>
 struct RowTile {
   static constexpr int CH = 16 / int(sizeof(T));
@@ -66,36 +79,38 @@ struct RowTile {
   static constexpr int CHUNKS = ROWS * NC;
   static constexpr int PER = (CHUNKS + NT - 1) / NT;
   uint4 r[PER];
-  int row[PER];
-  int col[PER];
 
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int it = threadIdx.x + u * NT;
-      row[u] = it < CHUNKS ? it / NC : ROWS;  // ROWS marks an idle slot
-      col[u] = (it % NC) * CH;
-    }
+  // chunk u of this thread: tile row and column (recomputed at each use
+  // instead of being held in registers across the loop)
+  static __device__ __forceinline__ int row_of(int u) {
+    const int it = threadIdx.x + u * NT;
+    return it < CHUNKS ? it / NC : ROWS;  // ROWS marks an idle slot
   }
+  static __device__ __forceinline__ int col_of(int u) { return ((threadIdx.x + u * NT) % NC) * CH; }
+
+  __device__ __forceinline__ void init() {}
   // rows row0 .. row0+ROWS-1 of `base` (token stride ts); rows >= nvalid -> 0
   __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ts, int row0, int nvalid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u);
       r[u] = make_uint4(0, 0, 0, 0);
-      if (row[u] < ROWS && row0 + row[u] < nvalid)
-        r[u] = *reinterpret_cast<const uint4*>(base + int64_t(row0 + row[u]) * ts + col[u]);
+      if (row < ROWS && row0 + row < nvalid)
+        r[u] = *reinterpret_cast<const uint4*>(base + int64_t(row0 + row) * ts + col_of(u));
     }
   }
   template <int P>
   __device__ __forceinline__ void store(T* __restrict__ lds) const {
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (row[u] < ROWS) {
+    for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u);
+      if (row < ROWS) {
+        const int off = row * P + col_of(u);
         if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint4*>(lds + row[u] * P + col[u]) = r[u];
+          *reinterpret_cast<uint4*>(lds + off) = r[u];
         } else {
           // odd fp32 pitch: rows are only 4-byte aligned
-          float* d = reinterpret_cast<float*>(lds) + row[u] * P + col[u];
+          float* d = reinterpret_cast<float*>(lds) + off;
           const float* s = reinterpret_cast<const float*>(&r[u]);
           d[0] = s[0];
           d[1] = s[1];
@@ -103,6 +118,7 @@ struct RowTile {
           d[3] = s[3];
         }
       }
+    }
   }
 };
 

@@ -6,41 +6,63 @@
 //   dq   = dq_acc + s * dC2P K_r      dk   = dk_acc + s * dP2C Q_r      (per token)
 //   dk_r = s * sum_t dC2P[t]^T Q[t]    dq_r = s * sum_t dP2C[t]^T K[t]    (per head)
 //
-// The token sums are split into fixed chunks; each chunk's [R, D] partial is
-// written to the workspace and a second kernel adds the chunks in index
-// order. No atomics; the chunking depends only on the shape.
-#include "tiles.hpp"
+// Both GEMMs stage row-major tiles with coalesced 16-byte loads; operands
+// that run down the rows are read with transposing LDS reads. The token sums
+// are split into fixed chunks; each chunk's [R, D] partial is written to the
+// workspace and a second kernel adds the chunks in index order. No atomics;
+// the chunking depends only on the shape.
+#include "pipe.hpp"
 
 namespace dfa {
 
 namespace {
 
+// Stage rows [row0, row0 + ROWS) x columns [col0, col0 + COLS) of a row-major
+// global matrix (row stride ld elements) into LDS (pitch P). Rows >= nrows or
+// columns >= ncols are zero; ncols and col0 are multiples of 16 bytes.
+template <typename T, int ROWS, int COLS, int P>
+__device__ __forceinline__ void stage(T* __restrict__ dst, const T* __restrict__ src, int64_t ld, int64_t row0,
+                                      int64_t nrows, int col0, int ncols) {
+  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int NC = COLS / CH;
+  for (int it = threadIdx.x; it < ROWS * NC; it += 256) {
+    const int r = it / NC, c = (it % NC) * CH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row0 + r < nrows && col0 + c < ncols) v = *reinterpret_cast<const uint4*>(src + (row0 + r) * ld + col0 + c);
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(dst + r * P + c) = v;
+    } else {
+      float* d = reinterpret_cast<float*>(dst) + r * P + c;
+      const float* f = reinterpret_cast<const float*>(&v);
+      d[0] = f[0];
+      d[1] = f[1];
+      d[2] = f[2];
+      d[3] = f[3];
+    }
+  }
+}
+
 // which = 0: dC2P with K_r into dq; which = 1: dP2C with Q_r into dk.
-// Workgroup: 128 tokens (4 waves x 32) x all D columns; loop over R in chunks
-// of RC rows, W^T chunk staged in LDS, strip rows read straight from global.
+// Workgroup: 128 tokens (4 waves x 32) x all D columns, R in chunks of 64.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void dx_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
-  using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, ND = D / 32;
-  constexpr int RC = 64;
-  constexpr int WTP = Pitch<T, RC>::rm;
-  __shared__ __align__(16) T Wt[D * WTP];
+  constexpr int KS = TR::KS, ND = D / 32;
+  constexpr int TM = 128, RC = 64;
+  constexpr int GP = RowPitch<T, RC>::rows, WP = RowPitch<T, D>::cols;
+  __shared__ __align__(16) T Gs[TM * GP];
+  __shared__ __align__(16) T Ws[RC * WP];
 
   const int which = blockIdx.z;
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
-  const int64_t t0 = int64_t(blockIdx.x) * 128 + wave * 32;
+  const int64_t t0 = int64_t(blockIdx.x) * TM;
   const int R = p.R, RP = p.RP;
   const T* G = (const T*)(which ? p.dp2c : p.dc2p) + int64_t(h) * p.T * RP;
   const T* W = (const T*)(which ? p.qr : p.kr) + int64_t(h) * R * D;
   const float* acc_in = (which ? p.dk_acc : p.dq_acc) + int64_t(h) * p.T * D;
   T* outp = (T*)(which ? p.dk : p.dq);
-
-  const int64_t ta = t0 + li;
-  const bool a_ok = ta < p.T;
-  const T* grow = G + (a_ok ? ta : 0) * RP;
 
   f32x16 acc[ND];
 #pragma unroll
@@ -48,22 +70,14 @@ __global__ __launch_bounds__(256) void dx_kernel(Params p) {
 
   for (int r0 = 0; r0 < R; r0 += RC) {
     __syncthreads();
-    stage_rows_tr<T, D, RC, WTP, WTP, 256>(nullptr, Wt, W, D, r0, R);
+    stage<T, TM, RC, GP>(Gs, G, RP, t0, p.T, r0, RP);
+    stage<T, RC, D, WP>(Ws, W, D, r0, R, 0, D);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < RC / KS; ++q) {
-      const int rr = r0 + q * KS + g * E;
-      frag a = (a_ok && rr < RP) ? TR::ld(grow + rr) : TR::zero();
+      const auto a = ld_row_fed<TR>(Gs, GP, wave * 32 + li, 0, q);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const T* wr = &Wt[(32 * nd + li) * WTP + q * KS + g * E];
-        frag b;
-        if constexpr (E == 8)
-          b = TR::ld2x4(wr, wr + 4);
-        else
-          b = TR::ld(wr);
-        acc[nd] = TR::mma(a, b, acc[nd]);
-      }
+      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Ws, WP, 0, 32 * nd, q), acc[nd]);
     }
   }
   // C[m = token][n = d]: lane holds column d = 32nd + li, rows acc_row(v, g)
@@ -71,7 +85,7 @@ __global__ __launch_bounds__(256) void dx_kernel(Params p) {
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t t = t0 + acc_row(v, g);
+      const int64_t t = t0 + wave * 32 + acc_row(v, g);
       if (t >= p.T) continue;
       const int c = 32 * nd + li;
       const float val = acc_in[t * D + c] + p.scale * acc[nd][v];
@@ -81,17 +95,16 @@ __global__ __launch_bounds__(256) void dx_kernel(Params p) {
 
 // Split-K partials of dk_r (which = 0: dC2P^T Q) and dq_r (which = 1: dP2C^T K).
 // Workgroup: 128 strip rows r (4 waves x 32) x all D columns, over one chunk
-// of tokens, TK tokens at a time; both operands staged transposed in LDS.
+// of tokens, TK tokens at a time.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void dw_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
-  using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, ND = D / 32;
-  constexpr int RM = 128, TK = 32;
-  constexpr int GTP = Pitch<T, TK>::rm;
-  __shared__ __align__(16) T Gt[RM * GTP];
-  __shared__ __align__(16) T Xt[D * GTP];
+  constexpr int KS = TR::KS, ND = D / 32;
+  constexpr int RM = 128, TK = 64;
+  constexpr int GP = RowPitch<T, RM>::cols, XP = RowPitch<T, D>::cols;
+  __shared__ __align__(16) T Gs[TK * GP];
+  __shared__ __align__(16) T Xs[TK * XP];
 
   const int which = blockIdx.z / p.H, h = blockIdx.z % p.H;
   const int chunk = blockIdx.y;
@@ -108,40 +121,15 @@ __global__ __launch_bounds__(256) void dw_kernel(Params p) {
   for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
 
   for (int64_t tk = c0; tk < c1; tk += TK) {
-    const int nv = int(c1 - tk);  // valid tokens in this step (>= 1)
     __syncthreads();
-    // Gt[r][t] from G rows t (RM columns starting at r0; columns >= RP -> 0)
-    {
-      constexpr int CH = 16 / sizeof(T);
-      for (int it = threadIdx.x; it < TK * (RM / CH); it += 256) {
-        const int t = it % TK, c = (it / TK) * CH;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (t < nv && r0 + c < RP) val = *reinterpret_cast<const uint4*>(G + (tk + t) * RP + r0 + c);
-        const T* ve = reinterpret_cast<const T*>(&val);
-#pragma unroll
-        for (int e = 0; e < CH; ++e) Gt[(c + e) * GTP + t] = ve[e];
-      }
-    }
-    stage_rows_tr<T, D, TK, GTP, GTP, 256>(nullptr, Xt, X + tk * p.ts, p.ts, 0, nv);
+    stage<T, TK, RM, GP>(Gs, G, RP, tk, c1, r0, RP);
+    stage<T, TK, D, XP>(Xs, X, p.ts, tk, c1, 0, D);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < TK / KS; ++q) {
-      const T* gr = &Gt[(32 * wave + li) * GTP + q * KS + g * E];
-      frag a;
-      if constexpr (E == 8)
-        a = TR::ld2x4(gr, gr + 4);
-      else
-        a = TR::ld(gr);
+      const auto a = ld_col<TR>(Gs, GP, 0, 32 * wave, q);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const T* xr = &Xt[(32 * nd + li) * GTP + q * KS + g * E];
-        frag b;
-        if constexpr (E == 8)
-          b = TR::ld2x4(xr, xr + 4);
-        else
-          b = TR::ld(xr);
-        acc[nd] = TR::mma(a, b, acc[nd]);
-      }
+      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Xs, XP, 0, 32 * nd, q), acc[nd]);
     }
   }
   float* part = p.part + ((int64_t(which) * p.H + h) * p.nchunk + chunk) * int64_t(R) * D;
@@ -191,23 +179,23 @@ void launch_sum_dt(const Params& p, hipStream_t st) {
   reduce_kernel<DT><<<unsigned((total + 255) / 256), 256, 0, st>>>(p);
 }
 
-#define DF_DISPATCH(FN, p, st)                                   \
-  switch (p.dtype) {                                             \
-    case DF_BF16_T:                                              \
-      if (p.D == 32) FN<DF_BF16_T, 32>(p, st);                   \
-      else if (p.D == 64) FN<DF_BF16_T, 64>(p, st);              \
-      else FN<DF_BF16_T, 128>(p, st);                            \
-      break;                                                     \
-    case DF_FP16_T:                                              \
-      if (p.D == 32) FN<DF_FP16_T, 32>(p, st);                   \
-      else if (p.D == 64) FN<DF_FP16_T, 64>(p, st);              \
-      else FN<DF_FP16_T, 128>(p, st);                            \
-      break;                                                     \
-    default:                                                     \
-      if (p.D == 32) FN<DF_FP32_T, 32>(p, st);                   \
-      else if (p.D == 64) FN<DF_FP32_T, 64>(p, st);              \
-      else FN<DF_FP32_T, 128>(p, st);                            \
-      break;                                                     \
+#define DF_DISPATCH(FN, p, st)                     \
+  switch (p.dtype) {                               \
+    case DF_BF16_T:                                \
+      if (p.D == 32) FN<DF_BF16_T, 32>(p, st);     \
+      else if (p.D == 64) FN<DF_BF16_T, 64>(p, st); \
+      else FN<DF_BF16_T, 128>(p, st);              \
+      break;                                       \
+    case DF_FP16_T:                                \
+      if (p.D == 32) FN<DF_FP16_T, 32>(p, st);     \
+      else if (p.D == 64) FN<DF_FP16_T, 64>(p, st); \
+      else FN<DF_FP16_T, 128>(p, st);              \
+      break;                                       \
+    default:                                       \
+      if (p.D == 32) FN<DF_FP32_T, 32>(p, st);     \
+      else if (p.D == 64) FN<DF_FP32_T, 64>(p, st); \
+      else FN<DF_FP32_T, 128>(p, st);              \
+      break;                                       \
   }
 
 }  // namespace
