@@ -122,4 +122,54 @@ struct RowTile {
   }
 };
 
+// A ROWS x COLS tile of a row-major matrix (row stride ld elements),
+// prefetched into registers by all NT threads (16-byte chunks) and committed
+// to a row-major LDS tile. Rows >= nrows and columns >= ncols load as zero
+// (ncols and the column offset are multiples of 16 bytes).
+template <typename T, int ROWS, int COLS, int NT>
+struct Tile2D {
+  static constexpr int CH = 16 / int(sizeof(T));
+  static constexpr int NC = COLS / CH;
+  static constexpr int CHUNKS = ROWS * NC;
+  static constexpr int PER = (CHUNKS + NT - 1) / NT;
+  uint4 r[PER];
+
+  static __device__ __forceinline__ int row_of(int u) {
+    const int it = threadIdx.x + u * NT;
+    return it < CHUNKS ? it / NC : ROWS;
+  }
+  static __device__ __forceinline__ int col_of(int u) { return ((threadIdx.x + u * NT) % NC) * CH; }
+
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t ld, int64_t row0, int64_t nrows, int col0,
+                                       int ncols) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u), c = col_of(u);
+      r[u] = make_uint4(0, 0, 0, 0);
+      if (row < ROWS && row0 + row < nrows && col0 + c < ncols)
+        r[u] = *reinterpret_cast<const uint4*>(src + (row0 + row) * ld + col0 + c);
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u);
+      if (row < ROWS) {
+        const int off = row * P + col_of(u);
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint4*>(lds + off) = r[u];
+        } else {
+          float* d = reinterpret_cast<float*>(lds) + off;
+          const float* f = reinterpret_cast<const float*>(&r[u]);
+          d[0] = f[0];
+          d[1] = f[1];
+          d[2] = f[2];
+          d[3] = f[3];
+        }
+      }
+    }
+  }
+};
+
 }  // namespace dfa

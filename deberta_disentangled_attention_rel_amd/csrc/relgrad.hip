@@ -6,8 +6,10 @@
 //   dq   = dq_acc + s * dC2P K_r      dk   = dk_acc + s * dP2C Q_r      (per token)
 //   dk_r = s * sum_t dC2P[t]^T Q[t]    dq_r = s * sum_t dP2C[t]^T K[t]    (per head)
 //
-// Both GEMMs stage row-major tiles with coalesced 16-byte loads; operands
-// that run down the rows are read with transposing LDS reads. The token sums
+// Both GEMMs stage row-major tiles with coalesced 16-byte loads, prefetching
+// the next tile into registers while the current one is multiplied (double-
+// buffered LDS, one barrier per step); operands that run down the rows are
+// read with transposing LDS reads. The token sums
 // are split into fixed chunks; each chunk's [R, D] partial is written to the
 // workspace and a second kernel adds the chunks in index order. No atomics;
 // the chunking depends only on the shape.
@@ -16,31 +18,6 @@
 namespace dfa {
 
 namespace {
-
-// Stage rows [row0, row0 + ROWS) x columns [col0, col0 + COLS) of a row-major
-// global matrix (row stride ld elements) into LDS (pitch P). Rows >= nrows or
-// columns >= ncols are zero; ncols and col0 are multiples of 16 bytes.
-template <typename T, int ROWS, int COLS, int P>
-__device__ __forceinline__ void stage(T* __restrict__ dst, const T* __restrict__ src, int64_t ld, int64_t row0,
-                                      int64_t nrows, int col0, int ncols) {
-  constexpr int CH = 16 / int(sizeof(T));
-  constexpr int NC = COLS / CH;
-  for (int it = threadIdx.x; it < ROWS * NC; it += 256) {
-    const int r = it / NC, c = (it % NC) * CH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < nrows && col0 + c < ncols) v = *reinterpret_cast<const uint4*>(src + (row0 + r) * ld + col0 + c);
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint4*>(dst + r * P + c) = v;
-    } else {
-      float* d = reinterpret_cast<float*>(dst) + r * P + c;
-      const float* f = reinterpret_cast<const float*>(&v);
-      d[0] = f[0];
-      d[1] = f[1];
-      d[2] = f[2];
-      d[3] = f[3];
-    }
-  }
-}
 
 // which = 0: dC2P with K_r into dq; which = 1: dP2C with Q_r into dk.
 // Workgroup: 128 tokens (4 waves x 32) x all D columns, R in chunks of 64.
@@ -51,8 +28,8 @@ __global__ __launch_bounds__(256) void dx_kernel(Params p) {
   constexpr int KS = TR::KS, ND = D / 32;
   constexpr int TM = 128, RC = 64;
   constexpr int GP = RowPitch<T, RC>::rows, WP = RowPitch<T, D>::cols;
-  __shared__ __align__(16) T Gs[TM * GP];
-  __shared__ __align__(16) T Ws[RC * WP];
+  __shared__ __align__(16) T Gs[2][TM * GP];
+  __shared__ __align__(16) T Ws[2][RC * WP];
 
   const int which = blockIdx.z;
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
@@ -64,21 +41,37 @@ __global__ __launch_bounds__(256) void dx_kernel(Params p) {
   const float* acc_in = (which ? p.dk_acc : p.dq_acc) + int64_t(h) * p.T * D;
   T* outp = (T*)(which ? p.dk : p.dq);
 
+  // the next R chunk is loaded into registers while the current one is
+  // multiplied, then written to the other LDS buffer (one barrier per chunk)
+  Tile2D<T, TM, RC, 256> gt;
+  Tile2D<T, RC, D, 256> wt;
+  const int nch = (R + RC - 1) / RC;
+  gt.load(G, RP, t0, p.T, 0, RP);
+  wt.load(W, D, 0, R, 0, D);
+  gt.template store<GP>(Gs[0]);
+  wt.template store<WP>(Ws[0]);
+  __syncthreads();
+
   f32x16 acc[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
-
-  for (int r0 = 0; r0 < R; r0 += RC) {
-    __syncthreads();
-    stage<T, TM, RC, GP>(Gs, G, RP, t0, p.T, r0, RP);
-    stage<T, RC, D, WP>(Ws, W, D, r0, R, 0, D);
-    __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) {
+      gt.load(G, RP, t0, p.T, (c + 1) * RC, RP);
+      wt.load(W, D, (c + 1) * RC, R, 0, D);
+    }
 #pragma unroll
     for (int q = 0; q < RC / KS; ++q) {
-      const auto a = ld_row_fed<TR>(Gs, GP, wave * 32 + li, 0, q);
+      const auto a = ld_row_fed<TR>(Gs[buf], GP, wave * 32 + li, 0, q);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Ws, WP, 0, 32 * nd, q), acc[nd]);
+      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Ws[buf], WP, 0, 32 * nd, q), acc[nd]);
     }
+    if (c + 1 < nch) {
+      gt.template store<GP>(Gs[buf ^ 1]);
+      wt.template store<WP>(Ws[buf ^ 1]);
+    }
+    __syncthreads();
   }
   // C[m = token][n = d]: lane holds column d = 32nd + li, rows acc_row(v, g)
 #pragma unroll
@@ -103,8 +96,8 @@ __global__ __launch_bounds__(256) void dw_kernel(Params p) {
   constexpr int KS = TR::KS, ND = D / 32;
   constexpr int RM = 128, TK = 64;
   constexpr int GP = RowPitch<T, RM>::cols, XP = RowPitch<T, D>::cols;
-  __shared__ __align__(16) T Gs[TK * GP];
-  __shared__ __align__(16) T Xs[TK * XP];
+  __shared__ __align__(16) T Gs[2][TK * GP];
+  __shared__ __align__(16) T Xs[2][TK * XP];
 
   const int which = blockIdx.z / p.H, h = blockIdx.z % p.H;
   const int chunk = blockIdx.y;
@@ -116,21 +109,37 @@ __global__ __launch_bounds__(256) void dw_kernel(Params p) {
   const int64_t c0 = int64_t(chunk) * p.chunk_tokens;
   const int64_t c1 = c0 + p.chunk_tokens < p.T ? c0 + p.chunk_tokens : p.T;
 
+  // next token block in registers while the current one is multiplied
+  Tile2D<T, TK, RM, 256> gt;
+  Tile2D<T, TK, D, 256> xt;
   f32x16 acc[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
-
-  for (int64_t tk = c0; tk < c1; tk += TK) {
-    __syncthreads();
-    stage<T, TK, RM, GP>(Gs, G, RP, tk, c1, r0, RP);
-    stage<T, TK, D, XP>(Xs, X, p.ts, tk, c1, 0, D);
-    __syncthreads();
+  if (c0 < c1) {
+    gt.load(G, RP, c0, c1, r0, RP);
+    xt.load(X, p.ts, c0, c1, 0, D);
+    gt.template store<GP>(Gs[0]);
+    xt.template store<XP>(Xs[0]);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int64_t tk = c0; tk < c1; tk += TK, buf ^= 1) {
+    const bool more = tk + TK < c1;
+    if (more) {
+      gt.load(G, RP, tk + TK, c1, r0, RP);
+      xt.load(X, p.ts, tk + TK, c1, 0, D);
+    }
 #pragma unroll
     for (int q = 0; q < TK / KS; ++q) {
-      const auto a = ld_col<TR>(Gs, GP, 0, 32 * wave, q);
+      const auto a = ld_col<TR>(Gs[buf], GP, 0, 32 * wave, q);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Xs, XP, 0, 32 * nd, q), acc[nd]);
+      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Xs[buf], XP, 0, 32 * nd, q), acc[nd]);
     }
+    if (more) {
+      gt.template store<GP>(Gs[buf ^ 1]);
+      xt.template store<XP>(Xs[buf ^ 1]);
+    }
+    __syncthreads();
   }
   float* part = p.part + ((int64_t(which) * p.H + h) * p.nchunk + chunk) * int64_t(R) * D;
 #pragma unroll

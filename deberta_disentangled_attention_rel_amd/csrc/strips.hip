@@ -6,15 +6,18 @@
 //   p2cs[h][t][r] = s*log2(e) * K[t,h,:] . Q_r[h,r,:]
 //
 // stored in the working dtype, pre-scaled into the log2 domain the attention
-// kernels use, rows padded to RP. Columns 0 and R-1 (the rows every
-// far-field pair saturates to) are also written contiguously per head into
-// `ends` [4][H][T].
+// kernels use, rows padded to RP (columns R..RP-1 are zero). Columns 0 and
+// R-1 (the rows every far-field pair saturates to) are also written
+// contiguously per head into `ends` [4][H][T].
 //
-// One workgroup computes a 128-token x 64-row tile of one strip (blockIdx.z
-// selects strip and head): 4 waves, each 32 tokens x 2 MFMA column tiles,
-// K = D in one pass, operands straight from global memory. The tile is
-// converted in registers, staged in LDS and written back as whole 16-byte
-// chunks of each row (the kernel is bound by its HBM writes).
+// The kernel is bound by its HBM writes (2*H*T*RP elements). Each wave owns
+// 32*MT tokens and sweeps all R rows in 32-row chunks, computing the
+// transposed product C^T = K_r Q^T with 32x32 MFMAs: lane l then holds token
+// l % 32 of each token tile and, per register group, 4 consecutive rows, so
+// it stores 8 (16-bit) or 16 (fp32) contiguous bytes of its own strip row;
+// the 8 stores of a chunk complete each 64-byte run of a row back to back.
+// The token operand stays in registers for the whole sweep and every K_r /
+// Q_r fragment (read from L2) feeds MT MFMAs.
 #include "common.hpp"
 
 namespace dfa {
@@ -27,72 +30,85 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS;
-  constexpr int TM = 128, TN = 64;
-  constexpr int CH = 16 / int(sizeof(T));
-  constexpr int OP = TN + CH;  // LDS pitch of the output tile
-  __shared__ __align__(16) T tile[TM * OP];
+  constexpr int MT = D <= 64 ? 4 : 2;  // 32-token tiles per wave
+  constexpr int WT = 32 * MT;          // tokens per wave
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
   const int wave = threadIdx.x >> 6;
-  const int which = blockIdx.z / p.H, h = blockIdx.z % p.H;
-  const int64_t t0 = int64_t(blockIdx.x) * TM;
-  const int r0 = blockIdx.y * TN;
-  const T* A = (const T*)(which ? p.k : p.q);
-  const T* B = (const T*)(which ? p.qr : p.kr);
-  T* out = (T*)(which ? p.p2cs : p.c2ps);
+  const int which = blockIdx.y / p.H, h = blockIdx.y % p.H;
+  const int64_t tw = (int64_t(blockIdx.x) * 4 + wave) * WT;  // first token of this wave
+  if (tw >= p.T) return;
+  const T* A = (const T*)(which ? p.k : p.q);    // token operand [T,H,D]
+  const T* B = (const T*)(which ? p.qr : p.kr);  // relative rows [H,R,D]
+  T* out = (T*)(which ? p.p2cs : p.c2ps) + int64_t(h) * p.T * p.RP;
+  T* ends = (T*)p.ends + (which ? 2 : 0) * int64_t(p.H) * p.T + int64_t(h) * p.T;
 
-  const int64_t ta = t0 + wave * 32 + li;
-  const bool a_ok = ta < p.T;
-  const T* arow = A + (a_ok ? ta : 0) * p.ts + int64_t(h) * p.hs;
-  const T* brow[2];
-  bool b_ok[2];
+  // token fragments, resident for the whole sweep (rows past T read row T-1)
+  frag a[MT][NQ];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = r0 + 32 * nt + li;
-    b_ok[nt] = r < p.R;
-    brow[nt] = B + (int64_t(h) * p.R + (b_ok[nt] ? r : 0)) * D;
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = min(tw + 32 * m + li, p.T - 1);
+    const T* row = A + t * p.ts + int64_t(h) * p.hs;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) a[m][q] = TR::ld(row + q * KS + g * E);
   }
-  f32x16 acc[2] = {zero16(), zero16()};
+  const T* brel = B + int64_t(h) * p.R * D;
+  const int rlast = p.R - 1;
+
+  for (int r0 = 0; r0 < p.RP; r0 += 32) {
+    const int r = r0 + li;  // relative row fed by this lane
+    const bool rok = r < p.R;
+    f32x16 acc[MT];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    frag a = a_ok ? TR::ld(arow + q * KS + g * E) : TR::zero();
+    for (int m = 0; m < MT; ++m) acc[m] = zero16();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      frag b = b_ok[nt] ? TR::ld(brow[nt] + q * KS + g * E) : TR::zero();
-      acc[nt] = TR::mma(a, b, acc[nt]);
+    for (int q = 0; q < NQ; ++q) {
+      const frag b = rok ? TR::ld(brel + int64_t(r) * D + q * KS + g * E) : TR::zero();
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = TR::mma(b, a[m][q], acc[m]);
     }
-  }
-  // C[m = token][n = row]: lane holds row 32nt + li, tokens acc_row(v, g)
+    // C^T[r][t]: lane holds token tw + 32m + li, rows r0 + acc_row(v, g)
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int m = 0; m < MT; ++m) {
+      const int64_t t = tw + 32 * m + li;
+      if (t >= p.T) continue;
+      T* orow = out + t * p.RP + r0;
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      tile[(wave * 32 + acc_row(v, g)) * OP + 32 * nt + li] = TR::from_f(acc[nt][v] * p.scale_log2);
-  __syncthreads();
-
-  const int64_t HT = int64_t(p.H) * p.T;
-  T* ends = (T*)p.ends + (which ? 2 : 0) * HT + int64_t(h) * p.T;
-  T* obase = out + int64_t(h) * p.T * p.RP;
-  for (int it = threadIdx.x; it < TM * (TN / CH); it += 256) {
-    const int m = it / (TN / CH), c = (it % (TN / CH)) * CH;
-    const int64_t t = t0 + m;
-    if (t >= p.T || r0 + c >= p.RP) continue;
-    *reinterpret_cast<uint4*>(obase + t * p.RP + r0 + c) = *reinterpret_cast<const uint4*>(&tile[m * OP + c]);
-  }
-  if (threadIdx.x < TM) {
-    const int m = threadIdx.x;
-    const int64_t t = t0 + m;
-    if (t < p.T) {
-      if (r0 == 0) ends[t] = tile[m * OP];
-      const int last = p.R - 1 - r0;
-      if (last >= 0 && last < TN) ends[HT + t] = tile[m * OP + last];
+      for (int grp = 0; grp < 4; ++grp) {
+        const int rr = 8 * grp + 4 * g;  // rows rr..rr+3 of this chunk
+        if (r0 + rr >= p.RP) continue;
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t lo = uint32_t(TR::from_f(acc[m][4 * grp] * p.scale_log2)) |
+                              (uint32_t(TR::from_f(acc[m][4 * grp + 1] * p.scale_log2)) << 16);
+          const uint32_t hi = uint32_t(TR::from_f(acc[m][4 * grp + 2] * p.scale_log2)) |
+                              (uint32_t(TR::from_f(acc[m][4 * grp + 3] * p.scale_log2)) << 16);
+          *reinterpret_cast<uint2*>(orow + rr) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(orow + rr) =
+              make_float4(acc[m][4 * grp] * p.scale_log2, acc[m][4 * grp + 1] * p.scale_log2,
+                          acc[m][4 * grp + 2] * p.scale_log2, acc[m][4 * grp + 3] * p.scale_log2);
+        }
+      }
+      // the end columns, as stored in the strip
+      if (r0 == 0 && g == 0) ends[t] = TR::from_f(acc[m][0] * p.scale_log2);
+      if (rlast >= r0 && rlast < r0 + 32) {
+        const int k = rlast - r0;
+        if (g == ((k >> 2) & 1)) {
+          const int vr = 4 * (k >> 3) + (k & 3);
+          float x = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x = v == vr ? acc[m][v] : x;
+          ends[int64_t(p.H) * p.T + t] = TR::from_f(x * p.scale_log2);
+        }
+      }
     }
   }
 }
 
 template <int DT>
 void launch_strips_dt(const Params& p, hipStream_t st) {
-  dim3 grid(unsigned((p.T + 127) / 128), unsigned((p.R + 63) / 64), unsigned(2 * p.H));
+  const int wt = 32 * (p.D <= 64 ? 4 : 2);
+  dim3 grid(unsigned((p.T + 4 * wt - 1) / (4 * wt)), unsigned(2 * p.H));
   switch (p.D) {
     case 32: strip_kernel<DT, 32><<<grid, 256, 0, st>>>(p); break;
     case 64: strip_kernel<DT, 64><<<grid, 256, 0, st>>>(p); break;
