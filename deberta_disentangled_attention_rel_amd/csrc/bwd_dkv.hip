@@ -37,12 +37,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32, ES = int(sizeof(T));
+  constexpr bool DMA = ES == 2;  // 16-bit tiles go global -> LDS without registers
   constexpr int BN = 128, BM = 32 * NQT, NL = BM + BN - 1;
   constexpr int QP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;   // C2P window: one row per query
   constexpr int WPW = BM + 8, WPP = WinPitch<T, WPW>::v;  // P2C window: one row per key
   static_assert(NL <= 256, "one table entry per thread");
-  using QTile = RowTile<T, BM, D, 256>;
+  using QTile = RowTile<T, BM, D, 256, true>;  // queries half-major (walk order)
 
   __shared__ __align__(16) T Qs[2][BM * QP];
   __shared__ __align__(16) T dOs[2][BM * QP];
@@ -106,8 +107,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   auto prefetch = [&](int qb) {
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
-    qt.load(qbase, p.ts, i0, sq.len);
-    ot.load(dobase, p.ts, i0, sq.len);
+    if constexpr (DMA) {
+      // straight into the free LDS buffer (last read two tiles ago)
+      DmaTile<T, BM, D, QP, 256, true>::issue(Qs[qb & 1], qbase, p.ts, i0, sq.len);
+      DmaTile<T, BM, D, QP, 256, true>::issue(dOs[qb & 1], dobase, p.ts, i0, sq.len);
+    } else {
+      qt.load(qbase, p.ts, i0, sq.len);
+      ot.load(dobase, p.ts, i0, sq.len);
+    }
     if (tid < BM) {
       const int i = i0 + tid;
       const bool in = i < sq.len;
@@ -122,8 +129,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
   auto commit = [&](int buf) {
-    qt.template store<QP>(Qs[buf]);
-    ot.template store<QP>(dOs[buf]);
+    if constexpr (!DMA) {
+      qt.template store<QP>(Qs[buf]);
+      ot.template store<QP>(dOs[buf]);
+    }
     if (tid < BM) {
       uq_s[buf][tid] = ureg;
       dlt_s[buf][tid] = dreg;
@@ -137,13 +146,19 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     dVt[nd] = zero16();
     dKt[nd] = zero16();
   }
-  StripWalk<TR> walk;
-  walk.init((T*)p.dp2c + (int64_t(h) * T_ + tok_j) * RP, p.R, RP);
-  const bool walker = jin && g == 0;
+  const int R = p.R;
+  T* wrow = (T*)p.dp2c + (int64_t(h) * T_ + tok_j) * RP;  // this key's dP2C row
+  int rc = R;                                                // open run (half 0): none yet
+  float sc = 0.f;
+  if constexpr (NARROW) {
+    rc = lut_p(lut_entry(p, -(jin ? jw : 0)));  // row of query 0
+    if (jin && g == 0) walk_open<TR>(wrow, R, rc);
+  }
 
   const int nqb = (sq.len + BM - 1) / BM;
   prefetch(0);
   commit(0);
+  wait_vmem();
   __syncthreads();
 
   for (int qb = 0; qb < nqb; ++qb) {
@@ -169,6 +184,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     const char* wp = reinterpret_cast<const char*>(Wp) + jl * WPP * ES -
                      (NARROW && cls == TILE_BAND ? win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - jl])) : 0);
 
+    // band tiles: each lane group walks its own half of the queries (the
+    // tile is stored half-major, so those are its 16*NQT registers in order)
+    const int r1 = (cls == TILE_BAND && i0 + 16 * NQT < sq.len) ? lut_p(lut_s[buf][16 * NQT - jl + BN - 1]) / (NARROW ? ES : 1)
+                                                                 : -1;
+    WalkHalf wk = walk_begin(g, rc, sc, r1);
     float colsum = 0.f;
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
@@ -181,7 +201,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       float P[16], dS[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int il = 32 * u + acc_row(v, g);
+        const int il = half_major_partner<NQT>(u, g, v);
         float rel = uq_s[buf][il];
         if (cls == TILE_BAND) {
           const uint32_t e = lut_s[buf][il - jl + BN - 1];
@@ -207,29 +227,33 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           dKt[nd] = TR::mma(ld_col<TR>(Qs[buf], QP, 32 * u, 32 * nd, q), sb, dKt[nd]);
         }
       }
-      // dP2C: ordered walk over this subtile's queries
       if (cls != TILE_BAND) {
+        // far tiles: one row, one sum per tile
         float cs = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) cs += dS[v];
         colsum += cs + xor32(cs);
       } else {
-        float other[16];
+        // dP2C: this half's queries of the subtile, in order
 #pragma unroll
-        for (int v = 0; v < 16; ++v) other[v] = xor32(dS[v]);
-        if (walker) {
-#pragma unroll
-          for (int k = 0; k < 32; ++k) {
-            const int il = 32 * u + k;
-            if (i0 + il >= sq.len) break;
-            const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-            walk.step(lut_p(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), val);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int il = half_major_partner<NQT>(u, g, v);
+          walk_step<TR, NARROW>(wrow, R, wk, lut_p(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), dS[v],
+                                jin && i0 + il < sq.len);
         }
       }
     }
-    if (cls != TILE_BAND && walker) walk.step(cls == TILE_FAR_LEFT ? 0 : p.R - 1, colsum);
+    if (cls != TILE_BAND) {
+      if (jin && g == 0) {
+        walk_step<TR, NARROW>(wrow, R, wk, cls == TILE_FAR_LEFT ? 0 : R - 1, colsum);
+        rc = wk.r;
+        sc = wk.s;
+      }
+    } else {
+      walk_merge<TR>(wrow, R, g, wk, rc, sc, jin);
+    }
     if (qb + 1 < nqb) commit(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -244,7 +268,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       dvp[c] = TR::from_f(dVt[nd][v]);
       dkp[c] = dKt[nd][v] * p.scale;
     }
-  if (g == 0) walk.finish();
+  if (g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
 }
 
 template <int DT, int D, bool NARROW>

@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ND = D / 32, ES = int(sizeof(T));
+  constexpr bool DMA = ES == 2;  // 16-bit tiles go global -> LDS without registers
   constexpr int BM = 128, BN = 32 * NKT, NL = BM + BN - 1;
   constexpr int KP = RowPitch<T, D>::rows, VP = RowPitch<T, D>::cols;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
@@ -100,8 +101,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   auto prefetch = [&](int kb) {
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
-    kt.load(kbase, p.ts, j0, sq.len);
-    vt.load(vbase, p.ts, j0, sq.len);
+    if constexpr (DMA) {
+      // straight into the free LDS buffer (last read two tiles ago)
+      DmaTile<T, BN, D, KP, 256>::issue(Ks[kb & 1], kbase, p.ts, j0, sq.len);
+      DmaTile<T, BN, D, VP, 256>::issue(Vs[kb & 1], vbase, p.ts, j0, sq.len);
+    } else {
+      kt.load(kbase, p.ts, j0, sq.len);
+      vt.load(vbase, p.ts, j0, sq.len);
+    }
     if (tid < BN) {
       const int j = j0 + tid;
       const bool in = j < sq.len;
@@ -116,8 +123,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   };
 
   auto commit = [&](int buf) {
-    kt.template store<KP>(Ks[buf]);
-    vt.template store<VP>(Vs[buf]);
+    if constexpr (!DMA) {
+      kt.template store<KP>(Ks[buf]);
+      vt.template store<VP>(Vs[buf]);
+    }
     if (tid < BN) bj_s[buf][tid] = breg;
     if (tid < NL) lut_s[buf][tid] = lreg;
   };
@@ -130,6 +139,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   const int nkb = (sq.len + BN - 1) / BN;
   prefetch(0);
   commit(0);
+  wait_vmem();
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
@@ -240,6 +250,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       body(BoolC<false>{});
 
     if (kb + 1 < nkb) commit(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 

@@ -70,9 +70,35 @@ template <typename T, int W> struct RowPitch {
   static constexpr int cols = sizeof(T) == 2 ? W + 16 : W + 1;
 };
 
+// Half-major partner order. A block of 32*NS partners (keys or queries) is
+// processed as NS MFMA subtiles of 32; storing partner p at LDS row
+// half_major_slot(p) makes register v of lane group g in subtile t hold
+// partner half_major_partner(t, g, v) = 16*NS*g + 16t + v: lane group 0 holds
+// partners [0, 16NS) and group 1 [16NS, 32NS), each in increasing order of
+// (t, v). The fragment reads of the tile are unchanged; only the partner an
+// LDS row stands for changes.
+template <int NS>
+__device__ __forceinline__ constexpr int half_major_partner(int t, int g, int v) {
+  return 16 * NS * g + 16 * t + v;
+}
+// LDS row of partner p, and its inverse: the partner stored at LDS row
+// `slot` (slot = 32t + acc_row(v, g)).
+template <int NS>
+__device__ __forceinline__ constexpr int half_major_slot(int p) {
+  const int g = p / (16 * NS), t = (p % (16 * NS)) / 16, v = p % 16;
+  return 32 * t + acc_row(v, g);
+}
+template <int NS>
+__device__ __forceinline__ constexpr int half_major_at(int slot) {
+  const int t = slot >> 5, m = slot & 31;
+  const int g = (m >> 2) & 1, v = 4 * (m >> 3) + (m & 3);
+  return half_major_partner<NS>(t, g, v);
+}
+
 // A ROWS x D tile of one head of a [T,H,D] tensor, prefetched into registers
-// by all NT threads (16-byte chunks) and committed to a row-major LDS tile.
-template <typename T, int ROWS, int D, int NT>
+// by all NT threads (16-byte chunks) and committed to a row-major LDS tile
+// (tile row p at LDS row p, or half_major_slot(p) with HALF_MAJOR).
+template <typename T, int ROWS, int D, int NT, bool HALF_MAJOR = false>
 struct RowTile {
   static constexpr int CH = 16 / int(sizeof(T));
   static constexpr int NC = D / CH;
@@ -105,7 +131,7 @@ struct RowTile {
     for (int u = 0; u < PER; ++u) {
       const int row = row_of(u);
       if (row < ROWS) {
-        const int off = row * P + col_of(u);
+        const int off = (HALF_MAJOR ? half_major_slot<ROWS / 32>(row) : row) * P + col_of(u);
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint4*>(lds + off) = r[u];
         } else {
@@ -171,5 +197,46 @@ struct Tile2D {
     }
   }
 };
+
+// Asynchronous copy of a ROWS x D tile of one head of a [T,H,D] tensor of a
+// 16-bit type into a row-major LDS tile of pitch P elements (P a multiple of
+// 8) with LDS-DMA loads, which bypass registers: every lane's 16 bytes land
+// at the instruction's (wave-uniform) LDS address + 16 * lane, so the NT
+// threads fill consecutive 16-byte slots. Slot s is LDS row s / (P/8), chunk
+// s % (P/8); chunks past D/8 are row padding and load a duplicate of chunk 0.
+// LDS row n holds tile row n, or half_major_at(n) with HALF_MAJOR. Rows >=
+// nvalid re-read row nvalid - 1 (finite data; the kernels mask those rows
+// through their bias). Completion: s_waitcnt vmcnt(0) by every thread, then
+// a barrier.
+template <typename T, int ROWS, int D, int P, int NT, bool HALF_MAJOR = false>
+struct DmaTile {
+  static_assert(sizeof(T) == 2 && P % 8 == 0 && D % 8 == 0, "16-bit rows of whole 16-byte chunks");
+  static constexpr int PC = P / 8, NC = D / 8;
+  static constexpr int SLOTS = ROWS * PC;
+  static constexpr int NI = (SLOTS + NT - 1) / NT;
+
+  static __device__ __forceinline__ void issue(T* lds, const T* __restrict__ base, int64_t ts, int row0, int nvalid) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int s0 = k * NT + wave * 64;  // first slot of this wave's instruction
+      if (s0 >= SLOTS) break;             // wave-uniform
+      const int s = k * NT + int(threadIdx.x);
+      if (s < SLOTS) {
+        const int slot = s / PC, c = s % PC;
+        const int row = HALF_MAJOR ? half_major_at<ROWS / 32>(slot) : slot;  // tile row stored at this LDS row
+        const int r = min(row0 + row, nvalid - 1);
+        const T* src = base + int64_t(r) * ts + (c < NC ? c : 0) * 8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16,
+                                         0, 0);
+      }
+    }
+  }
+};
+
+// Wait for this thread's outstanding vector-memory loads, LDS-DMA included
+// (vmcnt(0); export and LDS counters left alone).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace dfa

@@ -3,18 +3,142 @@
 // dC2P[i, r] = sum over keys j with delta(i,j) = r of dS[i,j], and
 // dP2C[j, r] = sum over queries i with delta(j,i) = r of dS[i,j].
 // Walking a row's partners in increasing order, the index r never increases
-// (the bucket is monotone in i - j), so every r is a contiguous run. The walk
-// keeps the open run in registers, writes it when r changes, writes zeros for
-// any r the row skips, and after the last partner writes zeros for the rest
-// (and the row padding up to RP). Every element of the row is written exactly
-// once, in a fixed order, by the lane that owns the row: no atomics, no
-// initialisation of the strip, bitwise-reproducible.
+// (the bucket is monotone in i - j), so every r is a contiguous run. The
+// lane pair that owns a row (lanes l and l ^ 32) walks a tile's partners in
+// two halves at once (the tiles are stored half-major, so each lane group's
+// registers hold one contiguous half): half 0 takes the first half and
+// carries the row's open run across tiles; half 1 takes the second half and
+// holds back its first run (the "head"). A merge then joins half 0's open
+// run with half 1's head. A run is written when the walk leaves it, rows the
+// walk skips are written as zeros, and after the last partner the open run,
+// the rows below it and the padding up to RP are written. Every element of
+// the row is written exactly once, in a fixed order, by one of the two lanes
+// that own the row: no atomics, no initialisation, bitwise-reproducible.
+//
+// NARROW (no table ever steps by more than one row): the walk never skips a
+// row, so a step is a compare, a predicated store and two selects. The rows
+// above the first partner's row are zeroed up front (walk_open), and the
+// open run always holds a real row.
 #pragma once
 
 #include "common.hpp"
 
 namespace dfa {
 
+// Write run (r_from, s) and zeros for the rows strictly between r_to and
+// r_from. r_from = R means "no run yet" (everything above r_to is still
+// unwritten); r_from < 0 means "nothing open" (write nothing).
+template <typename TR>
+__device__ __forceinline__ void walk_close(typename TR::T* row, int R, int r_from, float s, int r_to) {
+  if (r_from < 0) return;
+  if (r_from < R) row[r_from] = TR::from_f(s);
+  for (int rr = (r_from < R ? r_from : R) - 1; rr > r_to; --rr) row[rr] = TR::from_f(0.f);
+}
+
+// State of one half's walk through a tile.
+struct WalkHalf {
+  int r;      // open run row (-1: half 1 has met no partner yet)
+  float s;    // open run sum
+  bool headp; // half 1: the first run has not been closed yet
+  int rh;     // half 1: head row
+  float sh;   // half 1: head sum
+};
+
+// Start of a tile: half 0 continues the row's open run (rc, sc); half 1
+// starts at its first partner's row r1 (-1 when it has no partner).
+__device__ __forceinline__ WalkHalf walk_begin(int g, int rc, float sc, int r1) {
+  return g == 0 ? WalkHalf{rc, sc, false, -1, 0.f} : WalkHalf{r1, 0.f, true, -1, 0.f};
+}
+
+// One partner (row r, value v); a step with active == false changes nothing.
+template <typename TR, bool NARROW>
+__device__ __forceinline__ void walk_step(typename TR::T* row, int R, WalkHalf& w, int r, float v,
+                                          bool active = true) {
+  if constexpr (NARROW) {
+    // predicated: one masked store, no branches
+    const bool ch = active && r != w.r;
+    if (ch && !w.headp) row[w.r] = TR::from_f(w.s);
+    const bool hd = ch && w.headp;
+    w.rh = hd ? w.r : w.rh;
+    w.sh = hd ? w.s : w.sh;
+    w.headp = w.headp && !ch;
+    w.s = ch ? v : (active ? w.s + v : w.s);
+    w.r = active ? r : w.r;
+  } else {
+    if (!active) return;
+    if (r != w.r) {
+      if (w.headp) {
+        if (w.r >= 0) {  // close the head: hold its sum, zero the gap below it
+          w.rh = w.r;
+          w.sh = w.s;
+          w.headp = false;
+          for (int rr = w.r - 1; rr > r; --rr) row[rr] = TR::from_f(0.f);
+        }
+      } else {
+        walk_close<TR>(row, R, w.r, w.s, r);
+      }
+      w.r = r;
+      w.s = 0.f;
+    }
+    w.s += v;
+  }
+}
+
+// Join half 0's open run with what half 1 found; afterwards rc/sc hold the
+// row's open run (in half 0 lanes). Called by both halves (cross-lane
+// exchange inside), outside any lane-divergent branch.
+template <typename TR>
+__device__ __forceinline__ void walk_merge(typename TR::T* row, int R, int g, const WalkHalf& w, int& rc,
+                                           float& sc, bool owner) {
+  // half 1 publishes its head (or its only run) and its open tail run
+  const bool single = w.headp;
+  const int hr = single ? w.r : w.rh;
+  const float hs = single ? w.s : w.sh;
+  const int o_hr = __float_as_int(xor32(__int_as_float(hr)));
+  const float o_hs = xor32(hs);
+  const int o_tr = __float_as_int(xor32(__int_as_float(w.r)));
+  const float o_ts = xor32(w.s);
+  const int o_single = __float_as_int(xor32(__int_as_float(single ? 1 : 0)));
+  if (g != 0 || !owner) return;
+  if (o_hr < 0) {  // half 1 had no partners in this tile
+    rc = w.r;
+    sc = w.s;
+    return;
+  }
+  float merged = o_hs;
+  if (w.r == o_hr)
+    merged += w.s;
+  else
+    walk_close<TR>(row, R, w.r, w.s, o_hr);
+  if (o_single) {
+    rc = o_hr;
+    sc = merged;
+  } else {
+    row[o_hr] = TR::from_f(merged);
+    rc = o_tr;
+    sc = o_ts;
+  }
+}
+
+// Before the first tile (NARROW): zero the rows above the first partner's
+// row r_first, which becomes the open run.
+template <typename TR>
+__device__ __forceinline__ void walk_open(typename TR::T* row, int R, int r_first) {
+  for (int rr = R - 1; rr > r_first; --rr) row[rr] = TR::from_f(0.f);
+}
+
+// After the last tile: the open run, the rows below it and the padding.
+template <typename TR>
+__device__ __forceinline__ void walk_finish(typename TR::T* row, int R, int RP, int rc, float sc) {
+  walk_close<TR>(row, R, rc, sc, -1);
+  for (int rr = R; rr < RP; ++rr) row[rr] = TR::from_f(0.f);
+}
+
+// Single-walker form: the lane that owns the row (lane group 0) walks all of
+// a tile's partners; the other lane group hands over its accumulator rows.
+// The open run is kept in registers, written when r changes, with zeros for
+// any r the row skips; after the last partner the rest of the row (and its
+// padding up to RP) is written.
 template <typename TR>
 struct StripWalk {
   using T = typename TR::T;
@@ -50,7 +174,7 @@ struct StripWalk {
 };
 
 // Position of the k-th (0..31) row of a 32-row accumulator tile in the
-// register file: lane group k>>2 & 1, register 4*(k>>3) + (k&3).
+// register file: lane group (k >> 2) & 1, register 4*(k >> 3) + (k & 3).
 __device__ __forceinline__ constexpr int walk_grp(int k) { return (k >> 2) & 1; }
 __device__ __forceinline__ constexpr int walk_reg(int k) { return 4 * (k >> 3) + (k & 3); }
 
