@@ -53,6 +53,50 @@ def kernel_algorithmic_flops(stage, B, H, L, D, R):
     }.get(stage)
 
 
+# Sources each stage's kernel is built from: the committed HBM-traffic figure
+# of a kernel (profiles/hbm_traffic_<stage>_<workload>.md, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs) is reported only while these files hash to
+# the value recorded with it.
+_CSRC = os.path.join(ROOT, "deberta_disentangled_attention_rel_amd", "csrc")
+_COMMON = ["common.hpp", "params.hpp", "pipe.hpp", "band.hpp", "walk.hpp"]
+STAGE_SOURCES = {
+    "fwd": ["fwd.hip"] + _COMMON,
+    "bwd_dkv": ["bwd_dkv.hip"] + _COMMON,
+    "bwd_dq": ["bwd_dq.hip"] + _COMMON,
+    "strips": ["strips.hip", "common.hpp", "params.hpp"],
+}
+
+
+def stage_source_sha(stage):
+    import hashlib
+    files = STAGE_SOURCES.get(stage)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(stage, workload_name):
+    """HBM bytes per launch recorded for `stage`, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{stage}_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            rec[k.strip()] = v.strip().strip("`")
+    if rec.get("source_sha256") != stage_source_sha(stage):
+        return None
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp):
     """The float64 oracle on one (sequence, head) slice of the same workload."""
     import numpy as np
@@ -83,6 +127,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times), "
+                         "the reference for scaling memory counters to bytes")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -144,6 +191,14 @@ def main(argv=None) -> int:
     dom_ms = stages[dom][0] / stages[dom][1]
     dom_tf = kernel_algorithmic_flops(dom, B, H, L, D, R) / (dom_ms * 1e-3) / 1e12
     bound = "mfma"
+    if a.calib_copy_mib > 0:
+        nbytes = a.calib_copy_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -163,7 +218,8 @@ def main(argv=None) -> int:
         "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(dom, w.name)},
         "kernels": kern,
         "device": torch.cuda.get_device_properties(dev).name,
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
