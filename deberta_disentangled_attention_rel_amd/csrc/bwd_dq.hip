@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   constexpr int KP = RowPitch<T, D>::rows;
   constexpr int WC = BN + 8, WCP = WinPitch<T, WC>::v;
   static_assert(NL <= 256, "one table entry per thread");
-  using KTile = RowTile<T, BN, D, 256>;
+  using KTile = RowTile<T, BN, D, 256, true>;  // keys half-major (walk order)
 
   __shared__ __align__(16) T Ks[2][BN * KP];
   __shared__ __align__(16) T Vs[2][BN * KP];
@@ -125,9 +125,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   f32x16 dQt[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) dQt[nd] = zero16();
-  StripWalk<TR> walk;
-  walk.init((T*)p.dc2p + (int64_t(h) * T_ + tok_i) * RP, R, RP);
-  const bool walker = qin && g == 0;
+  T* wrow = (T*)p.dc2p + (int64_t(h) * T_ + tok_i) * RP;  // this query's dC2P row
+  int rc = R;                                                // open run (half 0): none yet
+  float sc = 0.f;
+  if constexpr (NARROW) {
+    rc = lut_c(lut_entry(p, qin ? iw : 0));  // row of key 0
+    if (qin && g == 0) walk_open<TR>(wrow, R, rc);
+  }
 
   const int nkb = (sq.len + BN - 1) / BN;
   prefetch(0);
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
           for (int t = 0; t < NKT; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int jl = 32 * t + acc_row(v, g);
+              const int jl = half_major_partner<NKT>(t, g, v);
               const uint32_t e = lrow[-jl];
               rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
                                    buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
           for (int t = 0; t < NKT; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int jl = 32 * t + acc_row(v, g);
+              const int jl = half_major_partner<NKT>(t, g, v);
               const uint32_t e = lrow[-jl];
               const int jj = min(j0 + jl, sq.len - 1);
               rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
@@ -186,9 +190,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][32 * t + acc_row(v, g)];
+          for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][half_major_partner<NKT>(t, g, v)];
       }
 
+      // band tiles: each lane group walks its own half of the keys (the tile
+      // is stored half-major, so those are its 16*NKT registers in order)
+      WalkHalf wk = walk_begin(g, rc, sc, -1);
+      if constexpr (BAND)
+        wk = walk_begin(g, rc, sc,
+                        j0 + 16 * NKT < sq.len ? lut_c(lut_s[buf][il - 16 * NKT + BN - 1]) / (NARROW ? ES : 1) : -1);
       float rowsum = 0.f;
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
@@ -218,22 +228,26 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
           for (int v = 0; v < 16; ++v) rs += dS[v];
           rowsum += rs + xor32(rs);
         } else {
-          // dC2P: ordered walk over this subtile's keys
-          float other[16];
+          // dC2P: this half's keys of the subtile, in order (a block of its
+          // own, so the scheduler keeps it apart from the next subtile)
+          if (qin) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) other[v] = xor32(dS[v]);
-          if (walker) {
-#pragma unroll
-            for (int k = 0; k < 32; ++k) {
-              if (j0 + 32 * t + k >= sq.len) break;
-              const float val = walk_grp(k) == 0 ? dS[walk_reg(k)] : other[walk_reg(k)];
-              walk.step(lut_c(lut_s[buf][il - 32 * t - k + BN - 1]) / (NARROW ? ES : 1), val);
+            for (int v = 0; v < 16; ++v) {
+              const int jl = half_major_partner<NKT>(t, g, v);
+              walk_step<TR, NARROW>(wrow, R, wk, lut_c(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), dS[v],
+                                    j0 + jl < sq.len);
             }
           }
         }
       }
       if constexpr (!BAND) {
-        if (walker) walk.step(cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+        if (qin && g == 0) {
+          walk_step<TR, NARROW>(wrow, R, wk, cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
+          rc = wk.r;
+          sc = wk.s;
+        }
+      } else {
+        walk_merge<TR>(wrow, R, g, wk, rc, sc, qin);
       }
     };
     if (cls == TILE_BAND)
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dqp[32 * nd + acc_row(v, g)] = dQt[nd][v] * p.scale;
-  if (g == 0) walk.finish();
+  if (g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
 }
 
 template <int DT, int D, bool NARROW>
