@@ -11,13 +11,14 @@
 // contiguously per head into `ends` [4][H][T].
 //
 // The kernel is bound by its HBM writes (2*H*T*RP elements). Each wave owns
-// 32*MT tokens and sweeps all R rows in 32-row chunks, computing the
-// transposed product C^T = K_r Q^T with 32x32 MFMAs: lane l then holds token
-// l % 32 of each token tile and, per register group, 4 consecutive rows, so
-// it stores 8 (16-bit) or 16 (fp32) contiguous bytes of its own strip row;
-// the 8 stores of a chunk complete each 64-byte run of a row back to back.
+// 32*MT tokens and sweeps all R rows in 64-row chunks, computing the
+// transposed product C^T = K_r Q^T with 32x32 MFMAs (lane l holds token
+// l % 32 of each token tile and, per register group, 4 consecutive rows).
 // The token operand stays in registers for the whole sweep and every K_r /
-// Q_r fragment (read from L2) feeds MT MFMAs.
+// Q_r fragment (read from L2) feeds MT MFMAs. Each 32-token x 64-row block is
+// staged in a wave-private LDS buffer and written back as whole 128-byte row
+// segments (8 rows per store instruction), so no cache line of the strip is
+// written in pieces.
 #include "common.hpp"
 
 namespace dfa {
@@ -30,8 +31,12 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS;
-  constexpr int MT = D <= 64 ? 4 : 2;  // 32-token tiles per wave
-  constexpr int WT = 32 * MT;          // tokens per wave
+  constexpr int MT = 2;        // 32-token tiles per wave
+  constexpr int WT = 32 * MT;  // tokens per wave
+  constexpr int RC = 64;       // rows per chunk
+  constexpr int CH = 16 / int(sizeof(T));
+  constexpr int SP = RC + CH;  // staging pitch (elements): rows stay 16-byte aligned
+  __shared__ __align__(16) T stage_s[4][32 * SP];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
   const int wave = threadIdx.x >> 6;
@@ -42,6 +47,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   const T* B = (const T*)(which ? p.qr : p.kr);  // relative rows [H,R,D]
   T* out = (T*)(which ? p.p2cs : p.c2ps) + int64_t(h) * p.T * p.RP;
   T* ends = (T*)p.ends + (which ? 2 : 0) * int64_t(p.H) * p.T + int64_t(h) * p.T;
+  T* st = stage_s[wave];
 
   // token fragments, resident for the whole sweep (rows past T read row T-1)
   frag a[MT][NQ];
@@ -55,51 +61,64 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   const T* brel = B + int64_t(h) * p.R * D;
   const int rlast = p.R - 1;
 
-  for (int r0 = 0; r0 < p.RP; r0 += 32) {
-    const int r = r0 + li;  // relative row fed by this lane
-    const bool rok = r < p.R;
-    f32x16 acc[MT];
+  for (int r0 = 0; r0 < p.RP; r0 += RC) {
+    f32x16 acc[MT][2];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = zero16();
+    for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = zero16();
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const frag b = rok ? TR::ld(brel + int64_t(r) * D + q * KS + g * E) : TR::zero();
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = r0 + 32 * rt + li;  // relative row fed by this lane
+      const bool rok = r < p.R;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = TR::mma(b, a[m][q], acc[m]);
+      for (int q = 0; q < NQ; ++q) {
+        const frag b = rok ? TR::ld(brel + int64_t(r) * D + q * KS + g * E) : TR::zero();
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][rt] = TR::mma(b, a[m][q], acc[m][rt]);
+      }
     }
-    // C^T[r][t]: lane holds token tw + 32m + li, rows r0 + acc_row(v, g)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int64_t t = tw + 32 * m + li;
-      if (t >= p.T) continue;
-      T* orow = out + t * p.RP + r0;
+      const int64_t tm = tw + 32 * m;
+      // C^T[r][t]: lane holds token tm + li, rows r0 + 32rt + 8grp + 4g + 0..3
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int rr = 8 * grp + 4 * g;  // rows rr..rr+3 of this chunk
-        if (r0 + rr >= p.RP) continue;
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = uint32_t(TR::from_f(acc[m][4 * grp] * p.scale_log2)) |
-                              (uint32_t(TR::from_f(acc[m][4 * grp + 1] * p.scale_log2)) << 16);
-          const uint32_t hi = uint32_t(TR::from_f(acc[m][4 * grp + 2] * p.scale_log2)) |
-                              (uint32_t(TR::from_f(acc[m][4 * grp + 3] * p.scale_log2)) << 16);
-          *reinterpret_cast<uint2*>(orow + rr) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(orow + rr) =
-              make_float4(acc[m][4 * grp] * p.scale_log2, acc[m][4 * grp + 1] * p.scale_log2,
-                          acc[m][4 * grp + 2] * p.scale_log2, acc[m][4 * grp + 3] * p.scale_log2);
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          T* d = st + li * SP + 32 * rt + 8 * grp + 4 * g;
+          const float x0 = acc[m][rt][4 * grp] * p.scale_log2, x1 = acc[m][rt][4 * grp + 1] * p.scale_log2;
+          const float x2 = acc[m][rt][4 * grp + 2] * p.scale_log2, x3 = acc[m][rt][4 * grp + 3] * p.scale_log2;
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<uint2*>(d) =
+                make_uint2(uint32_t(TR::from_f(x0)) | (uint32_t(TR::from_f(x1)) << 16),
+                           uint32_t(TR::from_f(x2)) | (uint32_t(TR::from_f(x3)) << 16));
+          } else {
+            *reinterpret_cast<float4*>(d) = make_float4(x0, x1, x2, x3);
+          }
+        }
+      // the end columns, as stored in the strip
+      const int64_t tl = tm + li;
+      if (tl < p.T) {
+        if (r0 == 0 && g == 0) ends[tl] = TR::from_f(acc[m][0][0] * p.scale_log2);
+        if (rlast >= r0 && rlast < r0 + RC) {
+          const int k = rlast - r0, rt = k >> 5, kk = k & 31;
+          if (g == ((kk >> 2) & 1)) {
+            const int vr = 4 * (kk >> 3) + (kk & 3);
+            float x = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x = v == vr ? (rt ? acc[m][1][v] : acc[m][0][v]) : x;
+            ends[int64_t(p.H) * p.T + tl] = TR::from_f(x * p.scale_log2);
+          }
         }
       }
-      // the end columns, as stored in the strip
-      if (r0 == 0 && g == 0) ends[t] = TR::from_f(acc[m][0] * p.scale_log2);
-      if (rlast >= r0 && rlast < r0 + 32) {
-        const int k = rlast - r0;
-        if (g == ((k >> 2) & 1)) {
-          const int vr = 4 * (k >> 3) + (k & 3);
-          float x = 0.f;
+      // wave-private buffer: a wave's LDS operations complete in order
+      // 32 rows x RC columns, RC/CH lanes per row, 64/(RC/CH) rows per instruction
+      constexpr int LPR = RC / CH, RPI = 64 / LPR;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) x = v == vr ? acc[m][v] : x;
-          ends[int64_t(p.H) * p.T + t] = TR::from_f(x * p.scale_log2);
-        }
+      for (int k = 0; k < 32 / RPI; ++k) {
+        const int row = k * RPI + lane / LPR, c = (lane % LPR) * CH;
+        const uint4 val = *reinterpret_cast<const uint4*>(st + row * SP + c);
+        const int64_t t = tm + row;
+        if (t < p.T && r0 + c < p.RP) *reinterpret_cast<uint4*>(out + t * p.RP + r0 + c) = val;
       }
     }
   }
@@ -107,7 +126,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
 
 template <int DT>
 void launch_strips_dt(const Params& p, hipStream_t st) {
-  const int wt = 32 * (p.D <= 64 ? 4 : 2);
+  const int wt = 64;
   dim3 grid(unsigned((p.T + 4 * wt - 1) / (4 * wt)), unsigned(2 * p.H));
   switch (p.D) {
     case 32: strip_kernel<DT, 32><<<grid, 256, 0, st>>>(p); break;
