@@ -52,7 +52,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   __shared__ __align__(16) T Vs[2][BN * VP];
   __shared__ __align__(16) float bj_s[2][BN];
   __shared__ uint32_t lut_s[2][NL];
-  __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
+  // C2P windows of band tiles: two LDS-DMA buffers filled one tile ahead
+  // (16-bit), or one buffer staged when the tile starts (fp32)
+  using Win = C2PWindowDma<uint16_t, BM, 256>;
+  constexpr bool AWIN = NARROW && DMA;
+  __shared__ __align__(16) T Wc[AWIN ? 2 : 1][AWIN ? Win::ELEMS : (NARROW ? BM * WCP : 1)];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
@@ -137,6 +141,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   float m = -INFINITY, l = 0.f;
 
   const int nkb = (sq.len + BN - 1) / BN;
+  [[maybe_unused]] Win win;
+  if constexpr (AWIN) {
+    // window of tile 0 now, row starts of tile 1 for the first iteration
+    if (cls_of(0) == TILE_BAND) {
+      win.load_starts(p, i0 - BN + 1);
+      win.issue(Wc[0], c2pstrip, RP, i0, sq.len);
+    }
+    if (nkb > 1 && cls_of(1) == TILE_BAND) win.load_starts(p, i0 - BN - BN + 1);
+  }
   prefetch(0);
   commit(0);
   wait_vmem();
@@ -146,13 +159,19 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     const int buf = kb & 1;
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
+    if constexpr (AWIN) {
+      // next band tile's window into the other buffer (free since the last
+      // barrier), then the row starts of the band tile after it
+      if (kb + 1 < nkb && cls_of(kb + 1) == TILE_BAND) win.issue(Wc[buf ^ 1], c2pstrip, RP, i0, sq.len);
+      if (kb + 2 < nkb && cls_of(kb + 2) == TILE_BAND) win.load_starts(p, i0 - (kb + 2) * BN - BN + 1);
+    }
     if (kb + 1 < nkb) prefetch(kb + 1);
 
     // the tile body, compiled once per tile class as straight-line code
     auto body = [&](auto band_c) {
       constexpr bool BAND = decltype(band_c)::value;
-      if constexpr (BAND && NARROW) {
-        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+      if constexpr (BAND && NARROW && !AWIN) {
+        stage_window<T, WC, WCP, 256>(Wc[0], c2pstrip, RP, BM, i0, sq.len,
                                       [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
         __syncthreads();
       }
@@ -167,7 +186,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
           // C2P from this row's LDS window; P2C straight from the strip in
           // L2 (for a fixed key the 32 lanes of a half read one contiguous
           // run of its strip row; keys past the sequence end read zero)
-          const char* wc = reinterpret_cast<const char*>(Wc) + il * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
+          const char* wc = reinterpret_cast<const char*>(Wc[AWIN ? buf : 0]) +
+                           (AWIN ? Win::row_offset(il) : il * WCP) * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
           const BufView prow = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
           const int soff = j0 * RP * ES;
 #pragma unroll
