@@ -192,6 +192,28 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     float colsum = 0.f;
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
+      // per-query terms of this subtile: the far C2P value minus the LSE, plus
+      // in band tiles the gathered C2P + P2C terms (one block per subtile, so
+      // the 16 gathers are in flight together)
+      float rel[16];
+      if (cls == TILE_BAND) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int il = half_major_partner<NQT>(u, g, v);
+          const uint32_t e = lut_s[buf][il - jl + BN - 1];
+          if constexpr (NARROW) {
+            rel[v] = TR::add2(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(Wc) + cb_s[il] + lut_c(e)),
+                              *reinterpret_cast<const T*>(wp + lut_p(e)), uq_s[buf][il]);
+          } else {
+            const int ii = min(i0 + il, sq.len - 1);
+            rel[v] = TR::add2(c2pstrip[int64_t(ii) * RP + lut_c(e)],
+                              p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)], uq_s[buf][il]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) rel[v] = uq_s[buf][half_major_partner<NQT>(u, g, v)];
+      }
       f32x16 S = zero16(), dP = zero16();
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
@@ -202,19 +224,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int il = half_major_partner<NQT>(u, g, v);
-        float rel = uq_s[buf][il];
-        if (cls == TILE_BAND) {
-          const uint32_t e = lut_s[buf][il - jl + BN - 1];
-          if constexpr (NARROW) {
-            rel = TR::add2(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(Wc) + cb_s[il] + lut_c(e)),
-                           *reinterpret_cast<const T*>(wp + lut_p(e)), rel);
-          } else {
-            const int ii = min(i0 + il, sq.len - 1);
-            rel = TR::add2(c2pstrip[int64_t(ii) * RP + lut_c(e)], p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)],
-                           rel);
-          }
-        }
-        P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel) + bj);
+        P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]) + bj);
         dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
       }
 #pragma unroll

@@ -58,6 +58,16 @@ template <> struct Tr<DF_BF16_T> {
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
   }
+  // c + the sum of a fragment's 8 elements (four packed dot products with (1, 1))
+  static __device__ __forceinline__ float sum(frag f, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const uint4 u = __builtin_bit_cast(uint4, f);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), ones, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), ones, c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), ones, c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), ones, c, false);
+  }
 };
 
 template <> struct Tr<DF_FP16_T> {
@@ -89,6 +99,15 @@ template <> struct Tr<DF_FP16_T> {
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
   }
+  static __device__ __forceinline__ float sum(frag f, float c) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const uint4 u = __builtin_bit_cast(uint4, f);
+    c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u.x), ones, c, false);
+    c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u.y), ones, c, false);
+    c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u.z), ones, c, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, u.w), ones, c, false);
+  }
 };
 
 template <> struct Tr<DF_FP32_T> {
@@ -105,6 +124,7 @@ template <> struct Tr<DF_FP32_T> {
   static __device__ __forceinline__ frag ld2x4(const T* p0, const T*) { return *p0; }
   static __device__ __forceinline__ frag zero() { return 0.f; }
   static __device__ __forceinline__ float add2(T a, T b, float c) { return (a + b) + c; }
+  static __device__ __forceinline__ float sum(frag f, float c) { return c + f; }
 };
 
 // ---------------------------------------------------------------------------

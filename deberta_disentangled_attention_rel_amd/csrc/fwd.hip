@@ -238,15 +238,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
       const float alpha = fast_exp2(m - msafe);
       const float shift = msafe - a;
-      float ls = 0.f;
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          y[t][v] = fast_exp2(y[t][v] - shift);
-          ls += y[t][v];
-        }
-      l = l * alpha + ls;
+        for (int v = 0; v < 16; ++v) y[t][v] = fast_exp2(y[t][v] - shift);
       m = mnew;
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -254,15 +249,18 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
 #pragma unroll
           for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
       }
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the row sum adds the same rounded P the MFMA uses
+      float ls = 0.f;
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q) {
           const frag pb = TR::pack(&y[t][q * E]);
+          ls = TR::sum(pb, ls);
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pb, O[nd]);
         }
+      l = l * alpha + ls;
     };
     if (cls == TILE_BAND)
       body(BoolC<true>{});
