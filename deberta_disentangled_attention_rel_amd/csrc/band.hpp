@@ -90,46 +90,34 @@ __device__ __forceinline__ void stage_window(T* __restrict__ dst, const T* __res
   }
 }
 
-// The C2P window of a band tile (one row of BN + 8 = 72 columns per query,
-// 16-bit types), filled by LDS-DMA one tile ahead of its use into one of two
-// buffers. Row il sits at element row_offset(il) = (9 il + il / 16) * 8: nine
-// 16-byte chunks per row and one padding chunk after every 16 rows, so lanes
-// reading different rows at nearby columns spread over the banks. The start
-// column of each row (its smallest C2P row in the tile, rounded down to 8)
-// comes from the index table in global memory, loaded one tile before the
-// copy is issued (load_starts), so issuing never waits on it.
-template <typename T, int ROWS, int NT>
-struct C2PWindowDma {
+// A strip window in LDS filled by LDS-DMA (16-bit types): ROWS rows of CPR
+// 16-byte chunks; with PAD16 one padding chunk follows every 16 rows, so lanes
+// reading different rows at nearby columns spread over the banks. Row r sits
+// at element row_offset(r). Slot s of the copy (16 bytes each, consecutive
+// lanes filling consecutive slots) holds chunk `chunk` of row `row` (row -1:
+// padding, loads a harmless duplicate).
+template <typename T, int ROWS, int CPR, bool PAD16, int NT>
+struct WinDma {
   static_assert(sizeof(T) == 2 && ROWS % 16 == 0, "16-bit rows, whole groups of 16");
-  static constexpr int CPR = 9;              // 16-byte chunks per row
-  static constexpr int GROUP = 16 * CPR + 1;  // 16 rows and one padding chunk
+  static constexpr int GROUP = 16 * CPR + (PAD16 ? 1 : 0);
   static constexpr int SLOTS = (ROWS / 16) * GROUP;
   static constexpr int NI = (SLOTS + NT - 1) / NT;
   static constexpr int ELEMS = SLOTS * 8;
-  int start[NI];  // start column of this thread's rows in the next window
 
-  static __device__ __forceinline__ constexpr int row_offset(int il) { return (il * CPR + il / 16) * 8; }
-  // row and chunk of slot s (row -1: padding)
+  static __device__ __forceinline__ constexpr int row_offset(int r) {
+    return (r * CPR + (PAD16 ? r / 16 : 0)) * 8;
+  }
   static __device__ __forceinline__ void slot(int s, int& row, int& chunk) {
     const int grp = s / GROUP, rem = s % GROUP;
-    row = rem == GROUP - 1 ? -1 : grp * 16 + rem / CPR;
-    chunk = rem == GROUP - 1 ? 0 : rem % CPR;
+    const bool pad = PAD16 && rem == 16 * CPR;
+    row = pad ? -1 : grp * 16 + rem / CPR;
+    chunk = pad ? 0 : rem % CPR;
   }
-  // rows of the tile whose smallest relative distance is dmin + row
-  __device__ __forceinline__ void load_starts(const Params& p, int dmin) {
-    const int off = p.Lmax - 1;
-#pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int s = k * NT + int(threadIdx.x);
-      int row, chunk;
-      slot(s, row, chunk);
-      const int d = dmin + (row < 0 ? 0 : row);
-      const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
-      start[k] = s < SLOTS ? (p.c2p[n] & ~7) : 0;
-    }
-  }
-  // copy the window of query rows row0.. (rows >= nvalid repeat row nvalid-1)
-  __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid) const {
+  // Copy strip rows row0 + r (clamped to nvalid - 1), columns from
+  // start_of(k, r) (a multiple of 8, k = this thread's instruction index).
+  template <class StartFn>
+  static __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid,
+                                               StartFn start_of) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
@@ -139,13 +127,45 @@ struct C2PWindowDma {
       if (s < SLOTS) {
         int row, chunk;
         slot(s, row, chunk);
-        const int r = min(row0 + (row < 0 ? 0 : row), nvalid - 1);
-        // columns past the strip row are never read; keep the copy in bounds
-        const int col = min(start[k] + chunk * 8, RP - 8);
+        const int rr = row < 0 ? 0 : row;
+        const int r = min(row0 + rr, nvalid - 1);
+        // chunks past the strip row are never read; keep the copy in bounds
+        const int col = min(start_of(k, rr) + chunk * 8, RP - 8);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(strip + int64_t(r) * RP + col),
                                          (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16, 0, 0);
       }
     }
+  }
+};
+
+// The forward's C2P window of a band tile (one row of BN + 8 = 72 columns per
+// query), copied one tile ahead into one of two buffers. The start column of
+// each row (its smallest C2P row in the tile, rounded down to 8) comes from
+// the index table in global memory, loaded one tile before the copy is issued
+// (load_starts), so issuing never waits on it.
+template <typename T, int ROWS, int NT>
+struct C2PWindowDma {
+  using W = WinDma<T, ROWS, 9, true, NT>;
+  static constexpr int NI = W::NI;
+  static constexpr int ELEMS = W::ELEMS;
+  int start[NI];  // start column of this thread's rows in the next window
+
+  static __device__ __forceinline__ constexpr int row_offset(int il) { return W::row_offset(il); }
+  // rows of the tile whose smallest relative distance is dmin + row
+  __device__ __forceinline__ void load_starts(const Params& p, int dmin) {
+    const int off = p.Lmax - 1;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int s = k * NT + int(threadIdx.x);
+      int row, chunk;
+      W::slot(s, row, chunk);
+      const int d = dmin + (row < 0 ? 0 : row);
+      const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
+      start[k] = s < W::SLOTS ? (p.c2p[n] & ~7) : 0;
+    }
+  }
+  __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid) const {
+    W::issue(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k]; });
   }
 };
 

@@ -50,8 +50,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   __shared__ __align__(16) float uq_s[2][BM];   // per-query (C2P end) - LSE*log2e, -inf if masked
   __shared__ __align__(16) float dlt_s[2][BM];
   __shared__ uint32_t lut_s[2][NL];
-  __shared__ __align__(16) T Wc[NARROW ? BM * WCP : 1];
-  __shared__ __align__(16) T Wp[NARROW ? BN * WPP : 1];
+  // strip windows of band tiles: 16-bit types copy the next band tile's
+  // windows by LDS-DMA halfway through the current tile, as soon as its last
+  // gather is done; fp32 stages them when the tile starts
+  constexpr bool AWIN = NARROW && DMA;
+  using WcW = WinDma<uint16_t, BM, WC / 8, false, 256>;  // one row per query (lanes read along it)
+  using WpW = WinDma<uint16_t, BN, WPW / 8, true, 256>;  // one row per key (lanes read across rows)
+  __shared__ __align__(16) T Wc[AWIN ? WcW::ELEMS : (NARROW ? BM * WCP : 1)];
+  __shared__ __align__(16) T Wp[AWIN ? WpW::ELEMS : (NARROW ? BN * WPP : 1)];
   __shared__ int cb_s[NARROW ? BM : 1];  // per query: byte base of its C2P window row
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
@@ -155,18 +161,36 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if (jin && g == 0) walk_open<TR>(wrow, R, rc);
   }
 
+  // windows of the band tile whose table slice is in lut_s[lb]
+  [[maybe_unused]] auto issue_windows = [&](int lb, int i0n) {
+    if constexpr (AWIN) {
+      WcW::issue(reinterpret_cast<uint16_t*>(Wc), reinterpret_cast<const uint16_t*>(c2pstrip), RP, i0n, sq.len,
+                 [&](int, int r) { return win_start_bytes<ES>(lut_c(lut_s[lb][r])) / ES; });
+      WpW::issue(reinterpret_cast<uint16_t*>(Wp), reinterpret_cast<const uint16_t*>(p2cstrip), RP, j0, sq.len,
+                 [&](int, int r) { return win_start_bytes<ES>(lut_p(lut_s[lb][NL - 1 - r])) / ES; });
+      if (tid < BM) cb_s[tid] = WcW::row_offset(tid) * ES - win_start_bytes<ES>(lut_c(lut_s[lb][tid]));
+    }
+  };
+
   const int nqb = (sq.len + BM - 1) / BM;
   prefetch(0);
   commit(0);
   wait_vmem();
   __syncthreads();
+  if constexpr (AWIN) {
+    if (cls_of(0) == TILE_BAND) {
+      issue_windows(0, 0);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
 
   for (int qb = 0; qb < nqb; ++qb) {
     const int buf = qb & 1;
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
     if (qb + 1 < nqb) prefetch(qb + 1);
-    if constexpr (NARROW) {
+    if constexpr (NARROW && !AWIN) {
       if (cls == TILE_BAND) {
         stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
                                       [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
@@ -181,7 +205,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if (cls == TILE_FAR_LEFT) bj = b_end0;
     if (cls == TILE_FAR_RIGHT) bj = b_end1;
     // byte base of this key's P2C window row
-    const char* wp = reinterpret_cast<const char*>(Wp) + jl * WPP * ES -
+    const char* wp = reinterpret_cast<const char*>(Wp) + (AWIN ? WpW::row_offset(jl) : jl * WPP) * ES -
                      (NARROW && cls == TILE_BAND ? win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - jl])) : 0);
 
     // band tiles: each lane group walks its own half of the queries (the
@@ -213,6 +237,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) rel[v] = uq_s[buf][half_major_partner<NQT>(u, g, v)];
+      }
+      if constexpr (AWIN) {
+        if (u == NQT - 1 && qb + 1 < nqb && cls_of(qb + 1) == TILE_BAND) {
+          // this tile's last gather is issued: publish the next tile's table
+          // slice, wait for every wave to be done with the windows, then copy
+          // the next tile's windows while this tile finishes
+          if (tid < NL) lut_s[buf ^ 1][tid] = lreg;
+          __syncthreads();
+          issue_windows(buf ^ 1, i0 + BM);
+        }
       }
       f32x16 S = zero16(), dP = zero16();
 #pragma unroll
