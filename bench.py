@@ -172,14 +172,38 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     df.profile_enable(True)
     df.profile_read()
+    # one event per step boundary on the stream the library launches on
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    marks[0].record()
+    for i in range(a.steps):
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     stages = df.profile_read()
     df.profile_enable(False)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(a.steps))
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+    # the two passes alone (outside the timed steps; the backward replays on
+    # the last forward's output and LSE)
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    fwd_ms = timed(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws), a.steps)
+    bwd_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
+                                  workspace=ws), a.steps)
 
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
@@ -216,6 +240,10 @@ def main(argv=None) -> int:
                    "tokens": B * L, "layout": "padded", "position_buckets": w.buckets,
                    "max_relative_positions": w.span, "rel_rows": R, "rel_rows_active": r_active},
         "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms": {"min": round(per_step[0], 4), "p10": round(pct(per_step, 0.1), 4),
+                    "median": round(pct(per_step, 0.5), 4), "p90": round(pct(per_step, 0.9), 4)},
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
