@@ -167,7 +167,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     }
     if (kb + 1 < nkb) prefetch(kb + 1);
 
-    // the tile body, compiled once per tile class as straight-line code
+    // the score part of the tile body (relative terms, S MFMAs, softmax),
+    // compiled once per tile class as straight-line code; it leaves the
+    // packed probabilities, their row sum and the rescale factor
+    frag pf[NKT][32 / KS];
+    float alpha, ls;
     auto body = [&](auto band_c) {
       constexpr bool BAND = decltype(band_c)::value;
       if constexpr (BAND && NARROW && !AWIN) {
@@ -236,36 +240,44 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       mt = fmaxf(mt, xor32(mt)) + a;
       const float mnew = fmaxf(m, mt);
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2(m - msafe);
+      const float m_old = m;
       const float shift = msafe - a;
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) y[t][v] = fast_exp2(y[t][v] - shift);
       m = mnew;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
-      }
-      // O^T += V^T P^T; the row sum adds the same rounded P the MFMA uses
-      float ls = 0.f;
+      alpha = fast_exp2(m_old - msafe);
+      // the row sum adds the same rounded P the MFMA uses
+      ls = 0.f;
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q) {
-          const frag pb = TR::pack(&y[t][q * E]);
-          ls = TR::sum(pb, ls);
-#pragma unroll
-          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pb, O[nd]);
+          pf[t][q] = TR::pack(&y[t][q * E]);
+          ls = TR::sum(pf[t][q], ls);
         }
-      l = l * alpha + ls;
     };
     if (cls == TILE_BAND)
       body(BoolC<true>{});
     else
       body(BoolC<false>{});
+
+    // O^T += V^T P^T after the lazy rescale (same code for both classes, so
+    // the accumulators are updated in place)
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[nd][v] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int q = 0; q < 32 / KS; ++q)
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
+    l = l * alpha + ls;
 
     if (kb + 1 < nkb) commit(buf ^ 1);
     wait_vmem();

@@ -8,41 +8,56 @@
 // sign(d) * (mid + ceil(x)), x = (mid-1) * ln(|d|/mid) / ln((span-1)/mid).
 // x is evaluated in fp64. When it lies within 1e-9 of an integer n, whether x
 // equals n exactly is decided in integers: x = n  <=>  (a/mid)^(mid-1) =
-// (b/mid)^n (a = |d|, b = span-1), compared prime by prime on the exponents.
+// (b/mid)^n (a = |d|, b = span-1), checked on the reduced numerators and
+// denominators through integer roots (a few operations, so the waves that
+// meet such a d do not hold the kernel up).
 #include "common.hpp"
 
 namespace dfa {
 
 namespace {
 
-__device__ int strip_factor(long long& x, long long p) {
-  int e = 0;
-  while (x % p == 0) {
-    x /= p;
-    ++e;
+__device__ unsigned gcd_u(unsigned a, unsigned b) {
+  while (b) {
+    const unsigned t = a % b;
+    a = b;
+    b = t;
   }
-  return e;
+  return a;
 }
 
-// (a/m)^(m-1) == (b/m)^n exactly?  <=>  for every prime p:
-// (m-1) * (v_p(a) - v_p(m)) == n * (v_p(b) - v_p(m)).
-__device__ bool exact_power_tie(long long a, long long b, long long m, long long n) {
-  long long x[3] = {a, b, m};
-  for (long long p = 2;; ++p) {
-    long long mx = x[0] > x[1] ? x[0] : x[1];
-    mx = mx > x[2] ? mx : x[2];
-    if (p * p > mx) break;
-    int ea = strip_factor(x[0], p), eb = strip_factor(x[1], p), em = strip_factor(x[2], p);
-    if ((m - 1) * (ea - em) != n * (eb - em)) return false;
+// w^e == target, computed exactly (stops as soon as the power passes target)
+__device__ bool power_is(unsigned long long w, unsigned e, unsigned long long target) {
+  unsigned long long x = 1;
+  for (unsigned i = 0; i < e; ++i) {
+    x *= w;
+    if (x > target) return false;
   }
-  // what is left of each number is 1 or a prime
-  for (int t = 0; t < 3; ++t) {
-    long long q = x[t];
-    if (q <= 1) continue;
-    int ea = x[0] == q, eb = x[1] == q, em = x[2] == q;
-    if ((m - 1) * (ea - em) != n * (eb - em)) return false;
+  return x == target;
+}
+
+// u^k == v^j for positive integers, k, j >= 1. With g = gcd(k, j) this holds
+// iff u = w^(j/g) and v = w^(k/g) for one integer w (unique factorisation).
+__device__ bool powers_equal(unsigned u, unsigned v, unsigned k, unsigned j) {
+  if (u == 1 || v == 1) return u == v;
+  const unsigned g = gcd_u(k, j), kk = k / g, jj = j / g;
+  const double w0 = rint(exp(log(double(u)) / double(jj)));
+  for (int dw = -1; dw <= 1; ++dw) {
+    const double w = w0 + dw;
+    if (w < 2.0) continue;
+    const unsigned long long wi = (unsigned long long)w;
+    if (power_is(wi, jj, u)) return power_is(wi, kk, v);
   }
-  return true;
+  return false;
+}
+
+// (a/m)^(m-1) == (b/m)^n exactly? Both fractions in lowest terms; the
+// equality holds iff it holds for the numerators and the denominators apart.
+__device__ bool exact_power_tie(unsigned a, unsigned b, unsigned m, long long n) {
+  if (n <= 0) return false;
+  const unsigned ga = gcd_u(a, m), gb = gcd_u(b, m);
+  const unsigned k = m - 1, j = unsigned(n);
+  return powers_equal(a / ga, b / gb, k, j) && powers_equal(m / ga, m / gb, k, j);
 }
 
 __device__ int bucket_of(int d, int span, int buckets) {
@@ -53,7 +68,7 @@ __device__ int bucket_of(int d, int span, int buckets) {
   const double x = double(mid - 1) * log(double(a) / double(mid)) / log(double(span - 1) / double(mid));
   const double n = rint(x);
   long long k;
-  if (fabs(x - n) <= 1e-9 * fmax(1.0, fabs(x)) && exact_power_tie(a, span - 1, mid, (long long)n))
+  if (fabs(x - n) <= 1e-9 * fmax(1.0, fabs(x)) && exact_power_tie(unsigned(a), unsigned(span - 1), unsigned(mid), (long long)n))
     k = (long long)n;
   else
     k = (long long)ceil(x);
@@ -68,8 +83,10 @@ __global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict_
   const int d = n - (Lmax - 1);
   const int att = buckets > 0 ? buckets : span;
   const int R = 2 * att;
-  int c = bucket_of(d, span, buckets) + att;
-  int p = bucket_of(-d, span, buckets) + att;
+  // bucket is odd, so the P2C row needs no second evaluation
+  const int b = bucket_of(d, span, buckets);
+  int c = b + att;
+  int p = att - b;
   c2p[n] = c < 0 ? 0 : (c > R - 1 ? R - 1 : c);
   p2c[n] = p < 0 ? 0 : (p > R - 1 ? R - 1 : p);
 }
