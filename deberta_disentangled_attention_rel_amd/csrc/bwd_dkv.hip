@@ -278,13 +278,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         for (int v = 0; v < 16; ++v) cs += dS[v];
         colsum += cs + xor32(cs);
       } else {
-        // dP2C: this half's queries of the subtile, in order
+        // dP2C: this half's queries of the subtile, in order (their rows
+        // are read in one batch, so the walk waits on LDS once)
+        int wr[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int il = half_major_partner<NQT>(u, g, v);
-          walk_step<TR, NARROW>(wrow, R, wk, lut_p(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), dS[v],
-                                jin && i0 + il < sq.len);
-        }
+        for (int v = 0; v < 16; ++v)
+          wr[v] = lut_p(lut_s[buf][half_major_partner<NQT>(u, g, v) - jl + BN - 1]) / (NARROW ? ES : 1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          walk_step<TR, NARROW>(wrow, R, wk, wr[v], dS[v], jin && i0 + half_major_partner<NQT>(u, g, v) < sq.len);
       }
     }
     if (cls != TILE_BAND) {

@@ -173,6 +173,26 @@ __device__ __forceinline__ T buf_load(BufView b, int voff, int soff) {
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(b.r, voff, soff, 0));
 }
 
+// Range-checked stores: a store whose bytes lie past the view is dropped by
+// the hardware. kBufSkip as the offset drops a store on purpose, so that a
+// guarded store needs no branch (and the wait counts around it stay exact).
+constexpr int kBufSkip = 0x7ff00000;
+template <typename T>
+__device__ __forceinline__ void buf_store(BufView b, int voff, T v) {
+  if constexpr (sizeof(T) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), b.r, voff, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), b.r, voff, 0, 0);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_store16(BufView b, int voff, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, b.r, voff, 0, 0);
+}
+__device__ __forceinline__ uint4 buf_load16(BufView b, int voff) {
+  const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, 0, 0);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
 // Compile-time flag passed to a generic lambda, so that a loop body can be
 // instantiated once per tile class (band / far) as straight-line code.
 template <bool B> struct BoolC {

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
-  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS;
+  constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ES = int(sizeof(T));
   constexpr int MT = 2;        // 32-token tiles per wave
   constexpr int WT = 32 * MT;  // tokens per wave
   constexpr int RC = 64;       // rows per chunk
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   __shared__ __align__(16) T stage_s[4][32 * SP];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: buffer views need it
   const int which = blockIdx.y / p.H, h = blockIdx.y % p.H;
   const int64_t tw = (int64_t(blockIdx.x) * 4 + wave) * WT;  // first token of this wave
   if (tw >= p.T) return;
@@ -58,28 +58,49 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) a[m][q] = TR::ld(row + q * KS + g * E);
   }
-  const T* brel = B + int64_t(h) * p.R * D;
   const int rlast = p.R - 1;
+  // Every memory operation of the sweep goes through a range-checked view
+  // with no branch around it: relative rows past R read zero, stores to
+  // tokens past T (or columns past RP) are dropped. With no conditional
+  // memory operations the compiler's wait counts stay exact, so waiting for
+  // the next chunk's fragments (loaded before this chunk's stores are
+  // issued; vector memory operations complete in issue order) never waits
+  // for the stores.
+  const int nt = int(min<int64_t>(WT, p.T - tw));  // tokens of this wave
+  const BufView bv = buf_view(B + int64_t(h) * p.R * D, uint32_t(p.R) * D * ES);
+  const BufView ov = buf_view(out + tw * p.RP, uint32_t(nt) * uint32_t(p.RP) * ES);
+  const BufView e0 = buf_view(ends + tw, uint32_t(nt) * ES);
+  const BufView e1 = buf_view(ends + int64_t(p.H) * p.T + tw, uint32_t(nt) * ES);
 
+  frag bf[2][NQ];
+  auto load_b = [&](int r0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = r0 + 32 * rt + li;  // relative row fed by this lane
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if constexpr (sizeof(T) == 2)
+          bf[rt][q] = __builtin_bit_cast(frag, buf_load16(bv, (r * D + q * KS + g * E) * ES));
+        else
+          bf[rt][q] = buf_load<T>(bv, (r * D + q * KS + g * E) * ES, 0);
+      }
+    }
+  };
+  load_b(0);
   for (int r0 = 0; r0 < p.RP; r0 += RC) {
     f32x16 acc[MT][2];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = zero16();
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int r = r0 + 32 * rt + li;  // relative row fed by this lane
-      const bool rok = r < p.R;
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const frag b = rok ? TR::ld(brel + int64_t(r) * D + q * KS + g * E) : TR::zero();
+      for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][rt] = TR::mma(b, a[m][q], acc[m][rt]);
-      }
-    }
+        for (int m = 0; m < MT; ++m) acc[m][rt] = TR::mma(bf[rt][q], a[m][q], acc[m][rt]);
+    if (r0 + RC < p.RP) load_b(r0 + RC);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int64_t tm = tw + 32 * m;
-      // C^T[r][t]: lane holds token tm + li, rows r0 + 32rt + 8grp + 4g + 0..3
+      // C^T[r][t]: lane holds token 32m + li, rows r0 + 32rt + 8grp + 4g + 0..3
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -96,20 +117,18 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
           }
         }
       // the end columns, as stored in the strip
-      const int64_t tl = tm + li;
-      if (tl < p.T) {
-        if (r0 == 0 && g == 0) ends[tl] = TR::from_f(acc[m][0][0] * p.scale_log2);
-        if (rlast >= r0 && rlast < r0 + RC) {
-          const int k = rlast - r0, rt = k >> 5, kk = k & 31;
-          if (g == ((kk >> 2) & 1)) {
-            const int vr = 4 * (kk >> 3) + (kk & 3);
-            float x = 0.f;
+      const int tl = 32 * m + li;
+      buf_store<T>(e0, r0 == 0 && g == 0 ? tl * ES : kBufSkip, TR::from_f(acc[m][0][0] * p.scale_log2));
+      float x = 0.f;
+      bool hit = false;
+      if (rlast >= r0 && rlast < r0 + RC) {
+        const int k = rlast - r0, rt = k >> 5, kk = k & 31;
+        hit = g == ((kk >> 2) & 1);
+        const int vr = 4 * (kk >> 3) + (kk & 3);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) x = v == vr ? (rt ? acc[m][1][v] : acc[m][0][v]) : x;
-            ends[int64_t(p.H) * p.T + tl] = TR::from_f(x * p.scale_log2);
-          }
-        }
+        for (int v = 0; v < 16; ++v) x = v == vr ? (rt ? acc[m][1][v] : acc[m][0][v]) : x;
       }
+      buf_store<T>(e1, hit ? tl * ES : kBufSkip, TR::from_f(x * p.scale_log2));
       // wave-private buffer: a wave's LDS operations complete in order
       // 32 rows x RC columns, RC/CH lanes per row, 64/(RC/CH) rows per instruction
       constexpr int LPR = RC / CH, RPI = 64 / LPR;
@@ -117,8 +136,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
       for (int k = 0; k < 32 / RPI; ++k) {
         const int row = k * RPI + lane / LPR, c = (lane % LPR) * CH;
         const uint4 val = *reinterpret_cast<const uint4*>(st + row * SP + c);
-        const int64_t t = tm + row;
-        if (t < p.T && r0 + c < p.RP) *reinterpret_cast<uint4*>(out + t * p.RP + r0 + c) = val;
+        buf_store16(ov, r0 + c < p.RP ? ((32 * m + row) * p.RP + r0 + c) * ES : kBufSkip, val);
       }
     }
   }
