@@ -26,6 +26,9 @@ CFLAGS = [
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wno-unused-result",
+    # per-thread arrays stay in registers (never silently moved to LDS, which
+    # would change a kernel's LDS budget and occupancy)
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

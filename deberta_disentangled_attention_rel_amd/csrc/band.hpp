@@ -148,7 +148,7 @@ struct C2PWindowDma {
   using W = WinDma<T, ROWS, 9, true, NT>;
   static constexpr int NI = W::NI;
   static constexpr int ELEMS = W::ELEMS;
-  int start[NI];  // start column of this thread's rows in the next window
+  int start[NI];  // smallest C2P row of this thread's rows in the next window
 
   static __device__ __forceinline__ constexpr int row_offset(int il) { return W::row_offset(il); }
   // rows of the tile whose smallest relative distance is dmin + row
@@ -161,11 +161,11 @@ struct C2PWindowDma {
       W::slot(s, row, chunk);
       const int d = dmin + (row < 0 ? 0 : row);
       const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
-      start[k] = s < W::SLOTS ? (p.c2p[n] & ~7) : 0;
+      start[k] = p.c2p[n];  // raw: rounded when the copy is issued, so nothing waits for it here
     }
   }
   __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid) const {
-    W::issue(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k]; });
+    W::issue(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k] & ~7; });
   }
 };
 

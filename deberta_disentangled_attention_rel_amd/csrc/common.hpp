@@ -58,6 +58,16 @@ template <> struct Tr<DF_BF16_T> {
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
   }
+  // two stored values in one register (a low, b high), and their sum plus c
+  static __device__ __forceinline__ uint32_t pair(T a, T b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, u16x2{a, b});
+  }
+  static __device__ __forceinline__ float add_pair(uint32_t pk, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
+  }
   // c + the sum of a fragment's 8 elements (four packed dot products with (1, 1))
   static __device__ __forceinline__ float sum(frag f, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -97,6 +107,15 @@ template <> struct Tr<DF_FP16_T> {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
+  }
+  static __device__ __forceinline__ uint32_t pair(T a, T b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, u16x2{a, b});
+  }
+  static __device__ __forceinline__ float add_pair(uint32_t pk, float c) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
   }
   static __device__ __forceinline__ float sum(frag f, float c) {
@@ -173,6 +192,10 @@ __device__ __forceinline__ T buf_load(BufView b, int voff, int soff) {
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(b.r, voff, soff, 0));
 }
 
+__device__ __forceinline__ uint32_t buf_load_u8(BufView b, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(b.r, voff, 0, 0);
+}
+
 // Range-checked stores: a store whose bytes lie past the view is dropped by
 // the hardware. kBufSkip as the offset drops a store on purpose, so that a
 // guarded store needs no branch (and the wait counts around it stay exact).
@@ -197,6 +220,11 @@ __device__ __forceinline__ uint4 buf_load16(BufView b, int voff) {
 // instantiated once per tile class (band / far) as straight-line code.
 template <bool B> struct BoolC {
   static constexpr bool value = B;
+};
+// Compile-time integer for the same purpose (e.g. the parity of a
+// double-buffered tile, so that each buffer is a distinct LDS object).
+template <int V> struct IntC {
+  static constexpr int value = V;
 };
 
 // Work-group placement over the 8 XCDs of the chip, each with its own L2.

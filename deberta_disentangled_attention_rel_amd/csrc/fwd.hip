@@ -48,15 +48,22 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   static_assert(NL <= 256, "one table entry per thread");
   using KTile = RowTile<T, BN, D, 256>;
 
-  __shared__ __align__(16) T Ks[2][BN * KP];
-  __shared__ __align__(16) T Vs[2][BN * VP];
+  // the two buffers of each tile are distinct LDS objects and every access
+  // names its buffer at compile time (the loop is unrolled by two): reads of
+  // the current buffer then provably do not alias the copy into the other
+  // one, so the compiler does not make them wait for that copy
+  __shared__ __align__(16) T Ks0[BN * KP];
+  __shared__ __align__(16) T Ks1[BN * KP];
+  __shared__ __align__(16) T Vs0[BN * VP];
+  __shared__ __align__(16) T Vs1[BN * VP];
   __shared__ __align__(16) float bj_s[2][BN];
   __shared__ uint32_t lut_s[2][NL];
   // C2P windows of band tiles: two LDS-DMA buffers filled one tile ahead
   // (16-bit), or one buffer staged when the tile starts (fp32)
   using Win = C2PWindowDma<uint16_t, BM, 256>;
   constexpr bool AWIN = NARROW && DMA;
-  __shared__ __align__(16) T Wc[AWIN ? 2 : 1][AWIN ? Win::ELEMS : (NARROW ? BM * WCP : 1)];
+  __shared__ __align__(16) T Wc0[AWIN ? Win::ELEMS : (NARROW ? BM * WCP : 1)];
+  __shared__ __align__(16) T Wc1[AWIN ? Win::ELEMS : 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
@@ -99,40 +106,50 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   KTile kt, vt;
   kt.init();
   vt.init();
-  float breg = 0.f;
-  uint32_t lreg = 0;
+  // the next tile's per-key values and table slice, loaded raw and only
+  // used when the tile is committed, so nothing waits for them (or for the
+  // tile copy issued after them) before then
+  T e_raw = TR::from_f(0.f);
+  uint32_t m_raw = 1u, c_raw = 0u, p_raw = 0u;
 
-  auto prefetch = [&](int kb) {
+  // Issue the loads of tile kb into buffer Q (free since the last barrier).
+  auto prefetch = [&](int kb, auto q_c) {
+    constexpr int Q = decltype(q_c)::value;
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
+    if (tid < BN) {
+      const int jc = min(j0 + tid, sq.len - 1);
+      m_raw = kmask ? kmask[jc] : 1u;
+      e_raw = ends[p2c_end_of(cls == TILE_BAND ? TILE_FAR_LEFT : cls) * HT + sq.start + jc];
+    }
+    if (tid < NL) {
+      const int off = p.Lmax - 1, d = i0 - j0 - BN + 1 + tid;
+      const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
+      c_raw = uint32_t(p.c2p[n]);
+      p_raw = uint32_t(p.p2c[n]);
+    }
     if constexpr (DMA) {
-      // straight into the free LDS buffer (last read two tiles ago)
-      DmaTile<T, BN, D, KP, 256>::issue(Ks[kb & 1], kbase, p.ts, j0, sq.len);
-      DmaTile<T, BN, D, VP, 256>::issue(Vs[kb & 1], vbase, p.ts, j0, sq.len);
+      DmaTile<T, BN, D, KP, 256>::issue(Q ? Ks1 : Ks0, kbase, p.ts, j0, sq.len);
+      DmaTile<T, BN, D, VP, 256>::issue(Q ? Vs1 : Vs0, vbase, p.ts, j0, sq.len);
     } else {
       kt.load(kbase, p.ts, j0, sq.len);
       vt.load(vbase, p.ts, j0, sq.len);
     }
-    if (tid < BN) {
-      const int j = j0 + tid;
-      const bool in = j < sq.len;
-      const int jc = in ? j : sq.len - 1;
-      const bool ok = in && (!kmask || kmask[jc]);
-      float b = 0.f;
-      if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
-      breg = ok ? b : -INFINITY;
-    }
-    if (cls == TILE_BAND && tid < NL)
-      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
   };
 
-  auto commit = [&](int buf) {
+  auto commit = [&](int kb, auto q_c) {
+    constexpr int Q = decltype(q_c)::value;
+    const int j0 = kb * BN;
+    const int cls = cls_of(kb);
     if constexpr (!DMA) {
-      kt.template store<KP>(Ks[buf]);
-      vt.template store<VP>(Vs[buf]);
+      kt.template store<KP>(Q ? Ks1 : Ks0);
+      vt.template store<VP>(Q ? Vs1 : Vs0);
     }
-    if (tid < BN) bj_s[buf][tid] = breg;
-    if (tid < NL) lut_s[buf][tid] = lreg;
+    if (tid < BN) {
+      const bool ok = j0 + tid < sq.len && m_raw != 0u;
+      bj_s[Q][tid] = ok ? (cls != TILE_BAND ? TR::to_f(e_raw) : 0.f) : -INFINITY;
+    }
+    if (tid < NL) lut_s[Q][tid] = NARROW ? (c_raw * ES | (p_raw * ES) << 16) : (c_raw | p_raw << 16);
   };
 
   f32x16 O[ND];
@@ -146,26 +163,35 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     // window of tile 0 now, row starts of tile 1 for the first iteration
     if (cls_of(0) == TILE_BAND) {
       win.load_starts(p, i0 - BN + 1);
-      win.issue(Wc[0], c2pstrip, RP, i0, sq.len);
+      win.issue(Wc0, c2pstrip, RP, i0, sq.len);
     }
     if (nkb > 1 && cls_of(1) == TILE_BAND) win.load_starts(p, i0 - BN - BN + 1);
   }
-  prefetch(0);
-  commit(0);
+  prefetch(0, IntC<0>{});
+  commit(0, IntC<0>{});
   wait_vmem();
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  // one tile; P = kb & 1 is the buffer it reads
+  auto iter = [&](int kb, auto p_c) {
+    constexpr int P = decltype(p_c)::value;
+    constexpr int buf = P;
+    const T* const Kc = P ? Ks1 : Ks0;
+    const T* const Vc = P ? Vs1 : Vs0;
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
-    if constexpr (AWIN) {
-      // next band tile's window into the other buffer (free since the last
-      // barrier), then the row starts of the band tile after it
-      if (kb + 1 < nkb && cls_of(kb + 1) == TILE_BAND) win.issue(Wc[buf ^ 1], c2pstrip, RP, i0, sq.len);
-      if (kb + 2 < nkb && cls_of(kb + 2) == TILE_BAND) win.load_starts(p, i0 - (kb + 2) * BN - BN + 1);
-    }
-    if (kb + 1 < nkb) prefetch(kb + 1);
+    // loads for the next tiles: the next band tile's window into the other
+    // buffer (free since the last barrier), the row starts of the band tile
+    // after it, the next K/V tile. Issued after this tile's own global
+    // gathers, so waiting for those never waits for these (vector memory
+    // operations complete in issue order).
+    auto issue_next = [&]() {
+      if constexpr (AWIN) {
+        if (kb + 1 < nkb && cls_of(kb + 1) == TILE_BAND) win.issue(P ? Wc0 : Wc1, c2pstrip, RP, i0, sq.len);
+        if (kb + 2 < nkb && cls_of(kb + 2) == TILE_BAND) win.load_starts(p, i0 - (kb + 2) * BN - BN + 1);
+      }
+      if (kb + 1 < nkb) prefetch(kb + 1, IntC<P ^ 1>{});
+    };
 
     // the score part of the tile body (relative terms, S MFMAs, softmax),
     // compiled once per tile class as straight-line code; it leaves the
@@ -175,7 +201,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     auto body = [&](auto band_c) {
       constexpr bool BAND = decltype(band_c)::value;
       if constexpr (BAND && NARROW && !AWIN) {
-        stage_window<T, WC, WCP, 256>(Wc[0], c2pstrip, RP, BM, i0, sq.len,
+        stage_window<T, WC, WCP, 256>(Wc0, c2pstrip, RP, BM, i0, sq.len,
                                       [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
         __syncthreads();
       }
@@ -190,19 +216,39 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
           // C2P from this row's LDS window; P2C straight from the strip in
           // L2 (for a fixed key the 32 lanes of a half read one contiguous
           // run of its strip row; keys past the sequence end read zero)
-          const char* wc = reinterpret_cast<const char*>(Wc[AWIN ? buf : 0]) +
+          const char* wc = reinterpret_cast<const char*>(AWIN && P ? Wc1 : Wc0) +
                            (AWIN ? Win::row_offset(il) : il * WCP) * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
           const BufView prow = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
           const int soff = j0 * RP * ES;
+          if constexpr (ES == 2) {
+            // both values of a key in one register (C2P low, P2C high)
+            uint32_t pr[NKT][16];
 #pragma unroll
-          for (int t = 0; t < NKT; ++t)
+            for (int t = 0; t < NKT; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int jl = 32 * t + acc_row(v, g);
-              const uint32_t e = lrow[-jl];
-              rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
-                                   buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
-            }
+              for (int v = 0; v < 16; ++v) {
+                const int jl = 32 * t + acc_row(v, g);
+                const uint32_t e = lrow[-jl];
+                pr[t][v] = TR::pair(*reinterpret_cast<const T*>(wc + lut_c(e)),
+                                    buf_load<T>(prow, jl * RP * ES + lut_p(e), soff));
+              }
+            issue_next();
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) rel[t][v] = TR::add_pair(pr[t][v], bj_s[buf][32 * t + acc_row(v, g)]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int jl = 32 * t + acc_row(v, g);
+                const uint32_t e = lrow[-jl];
+                rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
+                                     buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
+              }
+            issue_next();
+          }
         } else {
           const T* crow = c2pstrip + int64_t(qin ? iw : sq.len - 1) * RP;
 #pragma unroll
@@ -214,12 +260,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
               const int jj = min(j0 + jl, sq.len - 1);
               rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
             }
+          issue_next();
         }
       } else {
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
           for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][32 * t + acc_row(v, g)];
+        issue_next();
       }
 
       float y[NKT][16];
@@ -227,7 +275,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       for (int t = 0; t < NKT; ++t) {
         f32x16 acc = zero16();
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) acc = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], acc);
+        for (int q = 0; q < NQ; ++q) acc = TR::mma(ld_row<TR>(Kc, KP, 32 * t + li, q * KS + g * E), Qf[q], acc);
 #pragma unroll
         for (int v = 0; v < 16; ++v) y[t][v] = fmaf(acc[v], p.scale_log2, rel[t][v]);
       }
@@ -276,12 +324,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q)
 #pragma unroll
-        for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vs[buf], VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
+        for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vc, VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
     l = l * alpha + ls;
 
-    if (kb + 1 < nkb) commit(buf ^ 1);
+    if (kb + 1 < nkb) commit(kb + 1, IntC<P ^ 1>{});
     wait_vmem();
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    iter(kb, IntC<0>{});
+    if (kb + 1 < nkb) iter(kb + 1, IntC<1>{});
   }
 
   const float lt = l + xor32(l);
