@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   __syncthreads();
 
   // one tile; P = kb & 1 is the buffer it reads
-  auto iter = [&](int kb, auto p_c) {
+  auto iter = [&](int kb, auto p_c) __attribute__((always_inline)) {
     constexpr int P = decltype(p_c)::value;
     constexpr int buf = P;
     const T* const Kc = P ? Ks1 : Ks0;
