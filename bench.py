@@ -58,12 +58,12 @@ def kernel_algorithmic_flops(stage, B, H, L, D, R):
 # FETCH_SIZE / WRITE_SIZE runs) is reported only while these files hash to
 # the value recorded with it.
 _CSRC = os.path.join(ROOT, "deberta_disentangled_attention_rel_amd", "csrc")
-_COMMON = ["common.hpp", "params.hpp", "pipe.hpp", "band.hpp", "walk.hpp"]
+_COMMON = ["common.hpp", "params.hpp", "pipe.hpp", "band.hpp", "walk.hpp", "tiles.hpp", "../build.py"]
 STAGE_SOURCES = {
     "fwd": ["fwd.hip"] + _COMMON,
     "bwd_dkv": ["bwd_dkv.hip"] + _COMMON,
     "bwd_dq": ["bwd_dq.hip"] + _COMMON,
-    "strips": ["strips.hip", "common.hpp", "params.hpp"],
+    "strips": ["strips.hip", "common.hpp", "params.hpp", "../build.py"],
 }
 
 
@@ -124,7 +124,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
