@@ -154,6 +154,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   }
   const int R = p.R;
   T* wrow = (T*)p.dp2c + (int64_t(h) * T_ + tok_j) * RP;  // this key's dP2C row
+  // the dP2C rows of this work-group's keys, for the band-tile walk steps
+  const BufView wview = buf_view((T*)p.dp2c + (int64_t(h) * T_ + sq.start + j0) * RP,
+                                 uint32_t(min(BN, sq.len - j0)) * uint32_t(RP * ES));
+  const int wbase = jl * RP * ES;
   int rc = R;                                                // open run (half 0): none yet
   float sc = 0.f;
   if constexpr (NARROW) {
@@ -286,7 +290,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           wr[v] = lut_p(lut_s[buf][half_major_partner<NQT>(u, g, v) - jl + BN - 1]) / (NARROW ? ES : 1);
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          walk_step<TR, NARROW>(wrow, R, wk, wr[v], dS[v], jin && i0 + half_major_partner<NQT>(u, g, v) < sq.len);
+          if constexpr (NARROW)
+            walk_step_narrow<TR>(wview, wbase, wk, wr[v], dS[v], jin && i0 + half_major_partner<NQT>(u, g, v) < sq.len);
+          else
+            walk_step<TR, false>(wrow, R, wk, wr[v], dS[v], jin && i0 + half_major_partner<NQT>(u, g, v) < sq.len);
       }
     }
     if (cls != TILE_BAND) {

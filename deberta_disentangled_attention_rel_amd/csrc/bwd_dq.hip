@@ -126,6 +126,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) dQt[nd] = zero16();
   T* wrow = (T*)p.dc2p + (int64_t(h) * T_ + tok_i) * RP;  // this query's dC2P row
+  // the dC2P rows of this work-group's queries, for the band-tile walk steps
+  const BufView wview = buf_view((T*)p.dc2p + (int64_t(h) * T_ + sq.start + i0) * RP,
+                                 uint32_t(min(BM, sq.len - i0)) * uint32_t(RP * ES));
+  const int wbase = il * RP * ES;
   int rc = R;                                                // open run (half 0): none yet
   float sc = 0.f;
   if constexpr (NARROW) {
@@ -234,8 +238,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int jl = half_major_partner<NKT>(t, g, v);
-              walk_step<TR, NARROW>(wrow, R, wk, lut_c(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1), dS[v],
-                                    j0 + jl < sq.len);
+              const int r = lut_c(lut_s[buf][il - jl + BN - 1]) / (NARROW ? ES : 1);
+              if constexpr (NARROW)
+                walk_step_narrow<TR>(wview, wbase, wk, r, dS[v], j0 + jl < sq.len);
+              else
+                walk_step<TR, false>(wrow, R, wk, r, dS[v], j0 + jl < sq.len);
             }
           }
         }

@@ -84,6 +84,23 @@ __device__ __forceinline__ void walk_step(typename TR::T* row, int R, WalkHalf& 
   }
 }
 
+// The same NARROW step writing through a range-checked view of the rows of
+// a work-group (`rbase`: byte offset of this lane's row in the view): the
+// store is always issued, with an offset past the view when nothing is
+// written, so a step has no branch and no 64-bit address arithmetic.
+template <typename TR>
+__device__ __forceinline__ void walk_step_narrow(BufView rv, int rbase, WalkHalf& w, int r, float v, bool active) {
+  using T = typename TR::T;
+  const bool ch = active && r != w.r;
+  buf_store<T>(rv, ch && !w.headp ? rbase + w.r * int(sizeof(T)) : kBufSkip, TR::from_f(w.s));
+  const bool hd = ch && w.headp;
+  w.rh = hd ? w.r : w.rh;
+  w.sh = hd ? w.s : w.sh;
+  w.headp = w.headp && !ch;
+  w.s = ch ? v : (active ? w.s + v : w.s);
+  w.r = active ? r : w.r;
+}
+
 // Join half 0's open run with what half 1 found; afterwards rc/sc hold the
 // row's open run (in half 0 lanes). Called by both halves (cross-lane
 // exchange inside), outside any lane-divergent branch.
