@@ -58,16 +58,6 @@ template <> struct Tr<DF_BF16_T> {
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
   }
-  // two stored values in one register (a low, b high), and their sum plus c
-  static __device__ __forceinline__ uint32_t pair(T a, T b) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, u16x2{a, b});
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t pk, float c) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, c, false);
-  }
   // c + the sum of a fragment's 8 elements (four packed dot products with (1, 1))
   static __device__ __forceinline__ float sum(frag f, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -107,15 +97,6 @@ template <> struct Tr<DF_FP16_T> {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     const uint32_t pk = uint32_t(a) | (uint32_t(b) << 16);
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
-  }
-  static __device__ __forceinline__ uint32_t pair(T a, T b) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, u16x2{a, b});
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t pk, float c) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, c, false);
   }
   static __device__ __forceinline__ float sum(frag f, float c) {

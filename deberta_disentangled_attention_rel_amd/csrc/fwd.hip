@@ -182,9 +182,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     const int cls = cls_of(kb);
     // loads for the next tiles: the next band tile's window into the other
     // buffer (free since the last barrier), the row starts of the band tile
-    // after it, the next K/V tile. Issued after this tile's own global
-    // gathers, so waiting for those never waits for these (vector memory
-    // operations complete in issue order).
+    // after it, the next K/V tile
     auto issue_next = [&]() {
       if constexpr (AWIN) {
         if (kb + 1 < nkb && cls_of(kb + 1) == TILE_BAND) win.issue(P ? Wc0 : Wc1, c2pstrip, RP, i0, sq.len);
@@ -196,6 +194,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     // the score part of the tile body (relative terms, S MFMAs, softmax),
     // compiled once per tile class as straight-line code; it leaves the
     // packed probabilities, their row sum and the rescale factor
+    issue_next();
     frag pf[NKT][32 / KS];
     float alpha, ls;
     auto body = [&](auto band_c) {
@@ -220,35 +219,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
                            (AWIN ? Win::row_offset(il) : il * WCP) * ES - win_start_bytes<ES>(lut_c(lut_s[buf][il]));
           const BufView prow = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
           const int soff = j0 * RP * ES;
-          if constexpr (ES == 2) {
-            // both values of a key in one register (C2P low, P2C high)
-            uint32_t pr[NKT][16];
 #pragma unroll
-            for (int t = 0; t < NKT; ++t)
+          for (int t = 0; t < NKT; ++t)
 #pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int jl = 32 * t + acc_row(v, g);
-                const uint32_t e = lrow[-jl];
-                pr[t][v] = TR::pair(*reinterpret_cast<const T*>(wc + lut_c(e)),
-                                    buf_load<T>(prow, jl * RP * ES + lut_p(e), soff));
-              }
-            issue_next();
-#pragma unroll
-            for (int t = 0; t < NKT; ++t)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) rel[t][v] = TR::add_pair(pr[t][v], bj_s[buf][32 * t + acc_row(v, g)]);
-          } else {
-#pragma unroll
-            for (int t = 0; t < NKT; ++t)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int jl = 32 * t + acc_row(v, g);
-                const uint32_t e = lrow[-jl];
-                rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
-                                     buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
-              }
-            issue_next();
-          }
+            for (int v = 0; v < 16; ++v) {
+              const int jl = 32 * t + acc_row(v, g);
+              const uint32_t e = lrow[-jl];
+              rel[t][v] = TR::add2(*reinterpret_cast<const T*>(wc + lut_c(e)),
+                                   buf_load<T>(prow, jl * RP * ES + lut_p(e), soff), bj_s[buf][jl]);
+            }
         } else {
           const T* crow = c2pstrip + int64_t(qin ? iw : sq.len - 1) * RP;
 #pragma unroll
@@ -260,14 +239,12 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
               const int jj = min(j0 + jl, sq.len - 1);
               rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
             }
-          issue_next();
         }
       } else {
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
           for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][32 * t + acc_row(v, g)];
-        issue_next();
       }
 
       float y[NKT][16];
