@@ -31,9 +31,10 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   using T = typename TR::T;
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, NQ = D / KS, ES = int(sizeof(T));
-  constexpr int MT = 2;        // 32-token tiles per wave
+  constexpr int MT = 4;        // 32-token tiles per wave (4: measured best)
   constexpr int WT = 32 * MT;  // tokens per wave
   constexpr int RC = 64;       // rows per chunk
+  constexpr int NRT = RC / 32;  // 32-row tiles per chunk
   constexpr int CH = 16 / int(sizeof(T));
   constexpr int SP = RC + CH;  // staging pitch (elements): rows stay 16-byte aligned
   __shared__ __align__(16) T stage_s[4][32 * SP];
@@ -72,10 +73,10 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   const BufView e0 = buf_view(ends + tw, uint32_t(nt) * ES);
   const BufView e1 = buf_view(ends + int64_t(p.H) * p.T + tw, uint32_t(nt) * ES);
 
-  frag bf[2][NQ];
+  frag bf[NRT][NQ];
   auto load_b = [&](int r0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {
       const int r = r0 + 32 * rt + li;  // relative row fed by this lane
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
@@ -88,11 +89,13 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
   };
   load_b(0);
   for (int r0 = 0; r0 < p.RP; r0 += RC) {
-    f32x16 acc[MT][2];
+    f32x16 acc[MT][NRT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m][0] = acc[m][1] = zero16();
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < NRT; ++rt) acc[m][rt] = zero16();
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
     for (int m = 0; m < MT; ++m) {
       // C^T[r][t]: lane holds token 32m + li, rows r0 + 32rt + 8grp + 4g + 0..3
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           T* d = st + li * SP + 32 * rt + 8 * grp + 4 * g;
@@ -126,7 +129,9 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
         hit = g == ((kk >> 2) & 1);
         const int vr = 4 * (kk >> 3) + (kk & 3);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x = v == vr ? (rt ? acc[m][1][v] : acc[m][0][v]) : x;
+        for (int t = 0; t < NRT; ++t)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) x = (t == rt && v == vr) ? acc[m][t][v] : x;
       }
       buf_store<T>(e1, hit ? tl * ES : kBufSkip, TR::from_f(x * p.scale_log2));
       // wave-private buffer: a wave's LDS operations complete in order
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256) void strip_kernel(Params p) {
 
 template <int DT>
 void launch_strips_dt(const Params& p, hipStream_t st) {
-  const int wt = 64;
+  const int wt = 128;  // tokens per wave (32 * MT)
   dim3 grid(unsigned((p.T + 4 * wt - 1) / (4 * wt)), unsigned(2 * p.H));
   switch (p.D) {
     case 32: strip_kernel<DT, 32><<<grid, 256, 0, st>>>(p); break;
