@@ -204,6 +204,10 @@ def main(argv=None) -> int:
     fwd_ms = timed(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws), a.steps)
     bwd_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
                                   workspace=ws), a.steps)
+    # the inference forward (no LSE), into its own output buffer
+    out_inf = torch.empty_like(out)
+    inf_ms = timed(lambda: df.fwd_inference(q, k, v, q_r, k_r, w.span, w.buckets, out=out_inf, workspace=ws),
+                   a.steps)
 
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
@@ -244,6 +248,7 @@ def main(argv=None) -> int:
                     "median": round(pct(per_step, 0.5), 4), "p90": round(pct(per_step, 0.9), 4)},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "inference_fwd_ms": round(inf_ms, 4),
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),

@@ -17,14 +17,15 @@ from typing import Optional
 
 import torch
 
-__all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "bwd",
+__all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "fwd_inference", "bwd",
            "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
 DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
-            "df_attn_fwd", "df_attn_bwd", "df_strerror", "df_last_error", "df_attn_version",
+            "df_attn_fwd", "df_attn_fwd_inference", "df_attn_bwd", "df_strerror", "df_last_error",
+            "df_attn_version",
             "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name")
 NUM_STAGES = 9
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.df_build_rel_index.restype = ctypes.c_int
     L.df_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.df_attn_fwd.restype = ctypes.c_int
+    L.df_attn_fwd_inference.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.df_attn_fwd_inference.restype = ctypes.c_int
     L.df_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, vp, vp, sz, vp]
     L.df_attn_bwd.restype = ctypes.c_int
@@ -196,6 +199,25 @@ def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=No
                              int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
                              _ptr(out3), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
     return out.view(q.shape) if q.dim() == 4 else out, lse
+
+
+def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=None,
+                  max_seqlen: Optional[int] = None, out=None, workspace=None):
+    """Inference forward (no LSE, nothing kept for a backward). Returns ``out``."""
+    q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    shape = make_shape(q3, batch, L)
+    if out is None:
+        out = torch.empty_like(q3)
+    out3 = _as_thd(out)
+    if out3.shape != q3.shape or not out3.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    ws = _workspace(0, shape, span, buckets, q.device, workspace)
+    q_r, k_r = q_r.contiguous(), k_r.contiguous()
+    _check(lib().df_attn_fwd_inference(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r),
+                                       _ptr(k_r), int(span), int(buckets), _ptr(key_mask),
+                                       _ptr(cu_seqlens), _ptr(out3), _ptr(ws), ws.numel(),
+                                       _stream(q.device)))
+    return out.view(q.shape) if q.dim() == 4 else out
 
 
 def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=None,

@@ -326,16 +326,21 @@ int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets, int32_
   return rc ? rc : ok();
 }
 
-int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
-                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
-                const uint8_t* key_mask, const int32_t* cu_seqlens, void* out, float* lse,
-                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward on both entry points; lse == nullptr skips the LSE store.
+int fwd_impl(const df_attn_shape* shape, const void* q, const void* k, const void* v, const void* q_r,
+             const void* k_r, int32_t span, int32_t buckets, const uint8_t* key_mask,
+             const int32_t* cu_seqlens, void* out, float* lse, void* workspace, size_t workspace_bytes,
+             void* stream) {
   int att, R;
   int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
   if (rc) return rc;
   if ((rc = check_ptr(q, "q", 16)) || (rc = check_ptr(k, "k", 16)) || (rc = check_ptr(v, "v", 16)) ||
       (rc = check_ptr(q_r, "q_r", 16)) || (rc = check_ptr(k_r, "k_r", 16)) ||
-      (rc = check_ptr(out, "out", 16)) || (rc = check_ptr(lse, "lse", 4)))
+      (rc = check_ptr(out, "out", 16)) || (lse && (rc = check_ptr(lse, "lse", 4))))
     return rc;
   const Plan pl = make_plan(0, shape, R);
   if (workspace_bytes < pl.total)
@@ -357,6 +362,27 @@ int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const 
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
     return rc;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int df_attn_fwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens, void* out, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!lse) return fail(DF_ERR_INVALID, "lse is NULL (df_attn_fwd_inference is the forward without LSE)");
+  return fwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+int df_attn_fwd_inference(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                          const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                          const uint8_t* key_mask, const int32_t* cu_seqlens, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return fwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, nullptr, workspace,
+                  workspace_bytes, stream);
 }
 
 int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,

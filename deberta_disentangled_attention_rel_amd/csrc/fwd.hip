@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
     for (int v = 0; v < 16; ++v) op[32 * nd + acc_row(v, g)] = TR::from_f(O[nd][v] * inv);
-  if (g == 0) p.lse[int64_t(h) * T_ + tok_i] = ok ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  if (g == 0 && p.lse) p.lse[int64_t(h) * T_ + tok_i] = ok ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 template <int DT, int D, bool NARROW>

@@ -112,6 +112,20 @@ int df_attn_fwd(const df_attn_shape* shape,
                 void* out, float* lse,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Inference forward (DisentangledFlash 1.1.1 page, "Bundled H200 tuning
+ * profile": inference is a phase of its own, next to the training forward):
+ * the same computation as df_attn_fwd, writing out [T,H,D] only; no LSE and
+ * nothing for a backward pass is kept. Arguments, layouts, workspace
+ * (df_attn_workspace_size pass 0) and error codes as df_attn_fwd; the
+ * caller owns every buffer. */
+int df_attn_fwd_inference(const df_attn_shape* shape,
+                          const void* q, const void* k, const void* v,
+                          const void* q_r, const void* k_r,
+                          int32_t span, int32_t buckets,
+                          const uint8_t* key_mask, const int32_t* cu_seqlens,
+                          void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward pass: given the forward's out and lse and the output gradient
  * dout, writes dq, dk, dv [T,H,D] and dq_r, dk_r [H,R,D] (all dtype). The
  * gradients overwrite the outputs (never accumulate). Scores are recomputed

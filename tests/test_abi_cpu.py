@@ -117,6 +117,28 @@ def test_fwd_rejects_on_host(df):
     assert L.df_strerror(3).decode() == "workspace too small"
 
 
+def test_fwd_inference_rejects_on_host(df):
+    """The inference forward shares the forward's checks and takes no lse."""
+    L = df.lib()
+    s = _shape(df)
+    vp = [ctypes.c_void_p(FAKE)] * 6
+
+    def call(ptrs, ws_bytes=1 << 40, shape=s, span=512):
+        return L.df_attn_fwd_inference(ctypes.byref(shape), *ptrs[:5], span, 256, None, None, ptrs[5],
+                                       ctypes.c_void_p(FAKE), ws_bytes, None)
+    for k in range(6):
+        bad = list(vp)
+        bad[k] = None
+        assert call(bad) == 1
+        assert "NULL" in L.df_last_error().decode()
+    assert call(vp, ws_bytes=1024) == 3
+    assert call(vp, shape=_shape(df, total_tokens=200)) == 1
+    assert call(vp, span=0) == 1
+    # the training forward still requires lse
+    assert _fwd(df, s, [FAKE] * 6 + [0]) == 1
+    assert "df_attn_fwd_inference" in L.df_last_error().decode()
+
+
 def test_bwd_and_index_reject_on_host(df):
     L = df.lib()
     s = _shape(df)

@@ -114,3 +114,20 @@ def test_workload5_unbucketed_deterministic(dtype):
     again = _gpu(inp, True)
     for n in ("dq_r", "dk_r", "dq", "dk", "dv", "out", "lse"):
         assert np.array_equal(gpu[n].view(np.uint32), again[n].view(np.uint32)), n
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_inference_forward_full_size(n):
+    """The inference forward at full size equals the training forward's output
+    bit for bit (the same kernel without the LSE store); the training forward
+    is compared with the oracle by the tests above."""
+    import deberta_disentangled_attention_rel_amd as df
+    inp = workload_inputs(n, with_dout=False)
+    w = inp.workload
+    print(f"inference forward, workload {n}", flush=True)
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    out_t, _ = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
+    out_i = df.fwd_inference(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_i, out_t)

@@ -93,3 +93,26 @@ def test_backward_deterministic():
     b = run_gpu(inp)
     for n in ("out", "lse", "dq", "dk", "dv", "dq_r", "dk_r"):
         assert np.array_equal(a[n].view(np.uint32), b[n].view(np.uint32)), n
+
+
+# ----------------------------------------------------------------------------
+# inference forward: the training forward's output without LSE
+
+@pytest.mark.parametrize("name", ["bf16_D64_bucketed_ragged", "fp16_D128_unbucketed", "fp32_D64",
+                                  "bf16_packed_masked"])
+def test_inference_forward(name):
+    import deberta_disentangled_attention_rel_amd as df
+    from parity_util import to_dev, rel_l2, TOL
+    print(f"inference forward {name}", flush=True)
+    inp = _inp(**CASES[name])
+    w = inp.workload
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    out_t, _ = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
+    out_i = df.fwd_inference(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
+    torch.cuda.synchronize()
+    # the same kernel: bit-identical to the training forward's output
+    assert torch.equal(out_i, out_t)
+    ref = run_oracle(inp, backward=False)
+    err = rel_l2(out_i.float().cpu().numpy(), ref["out"])
+    assert np.isfinite(err) and err <= TOL[inp.dtype][0], err
