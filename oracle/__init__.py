@@ -9,3 +9,4 @@ from .df_oracle import (  # noqa: F401
     att_and_rows, bucket_exact, delta, rel_luts, sequences, scores,
     forward, backward, forward_rows, dq_rows,
 )
+from . import philox  # noqa: F401

@@ -179,14 +179,28 @@ def _probs(S: np.ndarray, valid: np.ndarray) -> tuple:
 # ----------------------------------------------------------------------------
 # forward
 
+def _dropout_factor(dropout, n, h, H, L):
+    """[L, L] factor keep / (1 - p) of attention dropout (1 where none), the
+    mask from ``philox.keep_mask`` (the DisentangledFlash page, "Status":
+    attention-probability dropout inside the fused kernels)."""
+    if dropout is None:
+        return 1.0
+    from . import philox
+    p, seed, offset = dropout
+    return philox.keep_mask(p, seed, offset, n, h, H, L) * (1.0 / (1.0 - p))
+
+
 def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
             cu_seqlens=None, batch=None, seqlen=None, return_probs: bool = False,
-            heads=None):
+            heads=None, dropout=None):
     """Output ``[T, H, D]`` and LSE ``[H, T]`` (natural log), float64.
 
     ``q, k, v`` are ``[T, H, D]``; ``q_r, k_r`` are ``[H, R, D]``.
     ``heads`` restricts the work to a subset of heads (other heads are left
     0 / -inf). With ``return_probs`` also returns ``{(seq, head): P}``.
+    ``dropout = (p, seed, offset)`` applies attention-probability dropout
+    after the softmax: out = (P * keep / (1 - p)) V; the LSE is that of the
+    undropped scores.
     """
     q, k, v, q_r, k_r = (np.asarray(x, dtype=np.float64) for x in (q, k, v, q_r, k_r))
     T, H, D = q.shape
@@ -201,7 +215,7 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
         for h in hs:
             S = scores(q[st:en, h], k[st:en, h], q_r[h], k_r[h], span, buckets)
             P, l = _probs(S, valid)
-            out[st:en, h] = P @ v[st:en, h]
+            out[st:en, h] = (P * _dropout_factor(dropout, n, h, H, en - st)) @ v[st:en, h]
             lse[h, st:en] = l
             if return_probs:
                 probs[(n, h)] = P
@@ -215,7 +229,7 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
 
 def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
              cu_seqlens=None, batch=None, seqlen=None, heads=None,
-             return_strips: bool = False):
+             return_strips: bool = False, dropout=None):
     """Gradients of ``sum(out * dout)``: ``dq, dk, dv, dq_r, dk_r``, float64.
 
     Follows the chain rule of the forward step by step: dV = P^T dO,
@@ -227,7 +241,9 @@ def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
     ``dK_r = s sum dC2P^T Q``, ``dQ_r = s sum dP2C^T K`` (sums over all
     sequences). ``heads`` restricts the work to a subset of heads (other heads
     are left zero). With ``return_strips`` also returns
-    ``{(seq, head): (dC2P, dP2C)}``.
+    ``{(seq, head): (dC2P, dP2C)}``. With ``dropout`` (see ``forward``) the
+    factor F = keep / (1 - p) enters as dV = (P F)^T dO and
+    dS = P (F dP - Delta), Delta_i = sum_j P_ij F_ij dP_ij (= dO_i . O_i).
     """
     q, k, v, q_r, k_r, dout = (np.asarray(x, dtype=np.float64)
                                for x in (q, k, v, q_r, k_r, dout))
@@ -252,8 +268,9 @@ def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
             Q, K, V, dO = q[st:en, h], k[st:en, h], v[st:en, h], dout[st:en, h]
             S = scores(Q, K, q_r[h], k_r[h], span, buckets)
             P, _ = _probs(S, valid)
-            dV = P.T @ dO
-            dP = dO @ V.T
+            F = _dropout_factor(dropout, n, h, H, L)
+            dV = (P * F).T @ dO
+            dP = (dO @ V.T) * F
             Delta = (P * dP).sum(axis=1)
             dS = P * (dP - Delta[:, None])
             # segmented sums (a scatter-add written with bincount)
