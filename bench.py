@@ -208,6 +208,16 @@ def main(argv=None) -> int:
     out_inf = torch.empty_like(out)
     inf_ms = timed(lambda: df.fwd_inference(q, k, v, q_r, k_r, w.span, w.buckets, out=out_inf, workspace=ws),
                    a.steps)
+    # a fwd+bwd step with attention dropout 0.1 (its own output buffers)
+    lse_d = torch.empty_like(lse)
+
+    def drop_step():
+        df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out_inf, lse=lse_d, workspace=ws,
+               dropout_p=0.1, seed=1234, offset=0)
+        df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out_inf, lse_d, dout, grads=grads, workspace=ws,
+               dropout_p=0.1, seed=1234, offset=0)
+    drop_step()
+    drop_ms = timed(drop_step, max(1, a.steps // 3))
 
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
@@ -249,6 +259,7 @@ def main(argv=None) -> int:
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "inference_fwd_ms": round(inf_ms, 4),
+        "dropout_0.1_step_ms": round(drop_ms, 4),
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),

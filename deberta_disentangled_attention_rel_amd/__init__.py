@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.
 DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
-            "df_attn_fwd", "df_attn_fwd_inference", "df_attn_bwd", "df_strerror", "df_last_error",
+            "df_attn_fwd", "df_attn_fwd_inference", "df_attn_bwd", "df_attn_fwd_dropout",
+            "df_attn_bwd_dropout", "df_strerror", "df_last_error",
             "df_attn_version",
             "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name")
 NUM_STAGES = 9
@@ -69,6 +70,12 @@ def lib() -> ctypes.CDLL:
     L.df_attn_fwd.restype = ctypes.c_int
     L.df_attn_fwd_inference.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     L.df_attn_fwd_inference.restype = ctypes.c_int
+    f32, u64, u32 = ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32
+    L.df_attn_fwd_dropout.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, u64, u32, vp, vp, vp, sz, vp]
+    L.df_attn_fwd_dropout.restype = ctypes.c_int
+    L.df_attn_bwd_dropout.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, u64, u32, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, vp, sz, vp]
+    L.df_attn_bwd_dropout.restype = ctypes.c_int
     L.df_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, vp, vp, sz, vp]
     L.df_attn_bwd.restype = ctypes.c_int
@@ -181,8 +188,11 @@ def _workspace(pass_, shape, span, buckets, device, workspace):
 
 
 def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=None,
-        max_seqlen: Optional[int] = None, out=None, lse=None, workspace=None):
-    """Forward pass. Returns ``(out, lse)`` with ``out`` shaped like ``q``."""
+        max_seqlen: Optional[int] = None, out=None, lse=None, workspace=None,
+        dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """Forward pass. Returns ``(out, lse)`` with ``out`` shaped like ``q``.
+    ``dropout_p > 0`` applies attention-probability dropout (mask from
+    ``(seed, offset)``; pass the same values to ``bwd``)."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
     shape = make_shape(q3, batch, L)
     T, H, D = q3.shape
@@ -195,9 +205,15 @@ def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=No
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     ws = _workspace(0, shape, span, buckets, q.device, workspace)
     q_r, k_r = q_r.contiguous(), k_r.contiguous()
-    _check(lib().df_attn_fwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
-                             int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
-                             _ptr(out3), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    if dropout_p:
+        _check(lib().df_attn_fwd_dropout(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r),
+                                         _ptr(k_r), int(span), int(buckets), _ptr(key_mask),
+                                         _ptr(cu_seqlens), float(dropout_p), int(seed), int(offset),
+                                         _ptr(out3), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
+    else:
+        _check(lib().df_attn_fwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
+                                 int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
+                                 _ptr(out3), _ptr(lse), _ptr(ws), ws.numel(), _stream(q.device)))
     return out.view(q.shape) if q.dim() == 4 else out, lse
 
 
@@ -221,8 +237,10 @@ def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_
 
 
 def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=None,
-        cu_seqlens=None, max_seqlen: Optional[int] = None, grads=None, workspace=None):
-    """Backward pass. Returns ``(dq, dk, dv, dq_r, dk_r)``."""
+        cu_seqlens=None, max_seqlen: Optional[int] = None, grads=None, workspace=None,
+        dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """Backward pass. Returns ``(dq, dk, dv, dq_r, dk_r)``. The dropout
+    arguments must be those of the forward that produced ``out``."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
     shape = make_shape(q3, batch, L)
     out3, dout3 = _as_thd(out).contiguous(), _as_thd(dout).contiguous()
@@ -235,11 +253,19 @@ def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=Non
             raise ValueError("dq, dk, dv must be contiguous tensors shaped like q")
     ws = _workspace(1, shape, span, buckets, q.device, workspace)
     q_r, k_r = q_r.contiguous(), k_r.contiguous()
-    _check(lib().df_attn_bwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
-                             int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
-                             _ptr(out3), _ptr(lse), _ptr(dout3), _ptr(_as_thd(dq)), _ptr(_as_thd(dk)),
-                             _ptr(_as_thd(dv)), _ptr(dq_r), _ptr(dk_r), _ptr(ws), ws.numel(),
-                             _stream(q.device)))
+    if dropout_p:
+        _check(lib().df_attn_bwd_dropout(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r),
+                                         _ptr(k_r), int(span), int(buckets), _ptr(key_mask),
+                                         _ptr(cu_seqlens), float(dropout_p), int(seed), int(offset),
+                                         _ptr(out3), _ptr(lse), _ptr(dout3), _ptr(_as_thd(dq)),
+                                         _ptr(_as_thd(dk)), _ptr(_as_thd(dv)), _ptr(dq_r), _ptr(dk_r),
+                                         _ptr(ws), ws.numel(), _stream(q.device)))
+    else:
+        _check(lib().df_attn_bwd(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r), _ptr(k_r),
+                                 int(span), int(buckets), _ptr(key_mask), _ptr(cu_seqlens),
+                                 _ptr(out3), _ptr(lse), _ptr(dout3), _ptr(_as_thd(dq)), _ptr(_as_thd(dk)),
+                                 _ptr(_as_thd(dv)), _ptr(dq_r), _ptr(dk_r), _ptr(ws), ws.numel(),
+                                 _stream(q.device)))
     if q.dim() == 4:
         dq, dk, dv = (x.view(q.shape) for x in (dq, dk, dv))
     return dq, dk, dv, dq_r, dk_r

@@ -330,11 +330,31 @@ int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets, int32_
 
 namespace {
 
-// The forward on both entry points; lse == nullptr skips the LSE store.
+struct Dropout {
+  float p;
+  uint64_t seed;
+  uint32_t offset;
+};
+
+// Dropout fields of the parameter block; DF_ERR_INVALID unless 0 <= p < 1.
+int set_dropout(dfa::Params& prm, const Dropout* d) {
+  if (!d || d->p == 0.f) return DF_OK;
+  if (!(d->p > 0.f && d->p < 1.f)) return fail(DF_ERR_INVALID, "dropout probability must be in [0, 1), got %g", double(d->p));
+  prm.drop = 1;
+  const double thr = std::floor(double(d->p) * 4294967296.0);
+  prm.drop_thr = thr >= 4294967295.0 ? 0xffffffffu : uint32_t(thr);
+  prm.drop_scale = float(1.0 / (1.0 - double(d->p)));
+  prm.seed_lo = uint32_t(d->seed);
+  prm.seed_hi = uint32_t(d->seed >> 32);
+  prm.drop_off = d->offset;
+  return DF_OK;
+}
+
+// The forward on every entry point; lse == nullptr skips the LSE store.
 int fwd_impl(const df_attn_shape* shape, const void* q, const void* k, const void* v, const void* q_r,
              const void* k_r, int32_t span, int32_t buckets, const uint8_t* key_mask,
              const int32_t* cu_seqlens, void* out, float* lse, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, const Dropout* drop = nullptr) {
   int att, R;
   int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
   if (rc) return rc;
@@ -355,6 +375,7 @@ int fwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   p.kr = k_r;
   p.out = out;
   p.lse = lse;
+  if ((rc = set_dropout(p, drop))) return rc;
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                      [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
@@ -385,11 +406,15 @@ int df_attn_fwd_inference(const df_attn_shape* shape, const void* q, const void*
                   workspace_bytes, stream);
 }
 
-int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
-                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
-                const uint8_t* key_mask, const int32_t* cu_seqlens, const void* out, const float* lse,
-                const void* dout, void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
-                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const void* v, const void* q_r,
+             const void* k_r, int32_t span, int32_t buckets, const uint8_t* key_mask,
+             const int32_t* cu_seqlens, const void* out, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, void* dq_r, void* dk_r, void* workspace, size_t workspace_bytes,
+             void* stream, const Dropout* drop) {
   int att, R;
   int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
   if (rc) return rc;
@@ -426,6 +451,7 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
   p.dc2p = ws + pl.dc2p;
   p.dp2c = ws + pl.dp2c;
   p.part = reinterpret_cast<float*>(ws + pl.part);
+  if ((rc = set_dropout(p, drop))) return rc;
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                        [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
@@ -444,6 +470,41 @@ int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const 
                      [&] { return dfa::launch_relgrad_sum(p, st); })))
     return rc;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int df_attn_bwd(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                const uint8_t* key_mask, const int32_t* cu_seqlens, const void* out, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, lse, dout, dq, dk, dv,
+                  dq_r, dk_r, workspace, workspace_bytes, stream, nullptr);
+}
+
+int df_attn_fwd_dropout(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                        uint32_t offset, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!lse) return fail(DF_ERR_INVALID, "lse is NULL");
+  const Dropout d{dropout_p, seed, offset};
+  return fwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, lse, workspace,
+                  workspace_bytes, stream, &d);
+}
+
+int df_attn_bwd_dropout(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                        uint32_t offset, const void* out, const float* lse, const void* dout, void* dq,
+                        void* dk, void* dv, void* dq_r, void* dk_r, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const Dropout d{dropout_p, seed, offset};
+  return bwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, lse, dout, dq, dk, dv,
+                  dq_r, dk_r, workspace, workspace_bytes, stream, &d);
 }
 
 }  // extern "C"

@@ -31,7 +31,7 @@ namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NQT, bool NARROW>
+template <int DT, int D, int NQT, bool NARROW, bool DROP>
 __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
@@ -263,7 +263,18 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       for (int v = 0; v < 16; ++v) {
         const int il = half_major_partner<NQT>(u, g, v);
         P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]) + bj);
-        dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
+        if constexpr (DROP) {
+          // this lane's key is word jw % 4 of the call for (query, key group):
+          // dV takes P F, dS = P (F dP - Delta), F = keep / (1 - p)
+          const Philox4 r = philox4x32_10(uint32_t(jw) >> 2, uint32_t(i0 + il), uint32_t(blk.z * p.H + h),
+                                          p.drop_off, p.seed_lo, p.seed_hi);
+          const uint32_t wd = (jw & 2) ? ((jw & 1) ? r.w[3] : r.w[2]) : ((jw & 1) ? r.w[1] : r.w[0]);
+          const float F = wd >= p.drop_thr ? p.drop_scale : 0.f;
+          dS[v] = P[v] * (dP[v] * F - dlt_s[buf][il]);
+          P[v] *= F;
+        } else {
+          dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
+        }
       }
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q) {
@@ -328,7 +339,10 @@ template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NQT = (DT == DF_FP32_T) ? 1 : 2;
-  dkv_kernel<DT, D, NQT, NARROW><<<grid, 256, 0, st>>>(p);
+  if (p.drop)
+    dkv_kernel<DT, D, NQT, NARROW, true><<<grid, 256, 0, st>>>(p);
+  else
+    dkv_kernel<DT, D, NQT, NARROW, false><<<grid, 256, 0, st>>>(p);
 }
 
 template <int DT, int D>

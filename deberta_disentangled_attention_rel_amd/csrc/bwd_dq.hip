@@ -29,7 +29,7 @@ namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NKT, bool NARROW>
+template <int DT, int D, int NKT, bool NARROW, bool DROP>
 __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
@@ -213,10 +213,28 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
           dP = TR::mma(ld_row<TR>(Vs[buf], KP, 32 * t + li, q * KS + g * E), dOf[q], dP);
         }
         float dS[16];
+        if constexpr (DROP) {
+          // dS = P (F dP - Delta), F = keep / (1 - p): registers 4k..4k+3
+          // hold four consecutive keys, one Philox call
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
-          dS[v] = P * (dP[v] - dlt);
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int j = j0 + half_major_partner<NKT>(t, g, 4 * k4);
+            const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h), p.drop_off,
+                                            p.seed_lo, p.seed_hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * k4 + e;
+              const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
+              const float F = r.w[e] >= p.drop_thr ? p.drop_scale : 0.f;
+              dS[v] = P * (dP[v] * F - dlt);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
+            dS[v] = P * (dP[v] - dlt);
+          }
         }
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q) {
@@ -279,7 +297,10 @@ template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
-  dq_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
+  if (p.drop)
+    dq_kernel<DT, D, NKT, NARROW, true><<<grid, 256, 0, st>>>(p);
+  else
+    dq_kernel<DT, D, NKT, NARROW, false><<<grid, 256, 0, st>>>(p);
 }
 
 template <int DT, int D>

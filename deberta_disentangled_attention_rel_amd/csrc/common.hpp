@@ -197,6 +197,39 @@ __device__ __forceinline__ uint4 buf_load16(BufView b, int voff) {
   return make_uint4(r.x, r.y, r.z, r.w);
 }
 
+// ---------------------------------------------------------------------------
+// Attention-probability dropout (DisentangledFlash 1.1.1 page, "Status": the
+// dropout runs inside the fused kernels and its Philox mask is regenerated in
+// the backward). Philox4x32 with 10 rounds, written from its definition
+// (Salmon, Moraes, Dror and Shaw, SC 2011): a round maps counter
+// (c0, c1, c2, c3) and key (k0, k1) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
+// hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key grows by (W0, W1) before every
+// round after the first. The pair (query i, key j) of sequence n, head h
+// draws word j % 4 of the call with counter (j / 4, i, n H + h, offset) and
+// key (seed low, seed high) and is kept iff that word >= the threshold.
+struct Philox4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
+    const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return {{c0, c1, c2, c3}};
+}
+
 // Compile-time flag passed to a generic lambda, so that a loop body can be
 // instantiated once per tile class (band / far) as straight-line code.
 template <bool B> struct BoolC {

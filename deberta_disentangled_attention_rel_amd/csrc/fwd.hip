@@ -35,7 +35,7 @@ namespace dfa {
 
 namespace {
 
-template <int DT, int D, int NKT, bool NARROW>
+template <int DT, int D, int NKT, bool NARROW, bool DROP>
 __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
@@ -282,6 +282,25 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
           pf[t][q] = TR::pack(&y[t][q * E]);
           ls = TR::sum(pf[t][q], ls);
         }
+      if constexpr (DROP) {
+        // the row sum above is of the undropped P; P V takes the dropped and
+        // rescaled P. Registers 4k..4k+3 of a subtile hold four consecutive
+        // keys, one Philox call.
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int j = j0 + 32 * t + acc_row(4 * k4, g);
+            const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h), p.drop_off,
+                                            p.seed_lo, p.seed_hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[t][4 * k4 + e] = r.w[e] >= p.drop_thr ? y[t][4 * k4 + e] * p.drop_scale : 0.f;
+          }
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int q = 0; q < 32 / KS; ++q) pf[t][q] = TR::pack(&y[t][q * E]);
+      }
     };
     if (cls == TILE_BAND)
       body(BoolC<true>{});
@@ -329,7 +348,10 @@ template <int DT, int D, bool NARROW>
 void launch_fwd_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
   constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
-  fwd_kernel<DT, D, NKT, NARROW><<<grid, 256, 0, st>>>(p);
+  if (p.drop)
+    fwd_kernel<DT, D, NKT, NARROW, true><<<grid, 256, 0, st>>>(p);
+  else
+    fwd_kernel<DT, D, NKT, NARROW, false><<<grid, 256, 0, st>>>(p);
 }
 
 template <int DT, int D>

@@ -42,6 +42,11 @@ struct Params {
   void* dc2p;               // [H][T][RP] dtype: segmented sums of dS over delta(i,j)
   void* dp2c;               // [H][T][RP] dtype: segmented sums of dS over delta(j,i)
   float* part;              // [2][H][nchunk][R][D] split-K partials
+  // attention-probability dropout (drop = 0: none)
+  int drop;
+  uint32_t drop_thr;        // a pair is kept iff its Philox word >= drop_thr
+  float drop_scale;         // 1 / (1 - p)
+  uint32_t seed_lo, seed_hi, drop_off;
   int nchunk;
   int chunk_tokens;
 };

@@ -139,6 +139,36 @@ int df_attn_bwd(const df_attn_shape* shape,
                 void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training forward and backward with attention-probability dropout
+ * (DisentangledFlash 1.1.1 page, "Status": the dropout runs inside the fused
+ * kernels and its Philox mask is regenerated in the backward instead of being
+ * stored). After the softmax each probability is kept with probability
+ * 1 - dropout_p and scaled by 1 / (1 - dropout_p), or set to 0; the LSE is
+ * that of the undropped scores. The mask is a function of (seed, offset) and
+ * the pair: for sequence n, head h, local query i and local key j, word j % 4
+ * of Philox4x32-10 with counter (j / 4, i, n * num_heads + h, offset) and key
+ * (seed mod 2^32, seed >> 32) keeps the pair iff it is >= floor(p * 2^32).
+ * The backward must be called with the forward's (dropout_p, seed, offset).
+ * Arguments otherwise as df_attn_fwd / df_attn_bwd; dropout_p must be in
+ * [0, 1) (DF_ERR_INVALID otherwise); dropout_p = 0 is the plain path. */
+int df_attn_fwd_dropout(const df_attn_shape* shape,
+                        const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r,
+                        int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens,
+                        float dropout_p, uint64_t seed, uint32_t offset,
+                        void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int df_attn_bwd_dropout(const df_attn_shape* shape,
+                        const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r,
+                        int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens,
+                        float dropout_p, uint64_t seed, uint32_t offset,
+                        const void* out, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of an error code. */
 const char* df_strerror(int code);
 

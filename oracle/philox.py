@@ -57,6 +57,8 @@ def keep_threshold(p: float) -> int:
 def keep_mask(p: float, seed: int, offset: int, n: int, h: int, H: int, L: int) -> np.ndarray:
     """Boolean [L, L] keep mask of sequence n, head h (rows: queries i, columns: keys j)."""
     thr = keep_threshold(p)
+    if L == 0:  # an empty sequence has no pairs
+        return np.zeros((0, 0), dtype=bool)
     i = np.arange(L, dtype=np.uint64)[:, None]
     jg = np.arange((L + 3) // 4, dtype=np.uint64)[None, :]
     words = philox4x32_10(jg, i, np.uint64(n * H + h), np.uint64(offset & _U32), seed & _U32,

@@ -139,6 +139,23 @@ def test_fwd_inference_rejects_on_host(df):
     assert "df_attn_fwd_inference" in L.df_last_error().decode()
 
 
+def test_dropout_entry_points_reject_on_host(df):
+    L = df.lib()
+    s = _shape(df)
+    vp = [ctypes.c_void_p(FAKE)] * 7
+    for p in (1.0, -0.1, float("nan")):
+        rc = L.df_attn_fwd_dropout(ctypes.byref(s), *vp[:5], 512, 256, None, None, p, 1, 0, vp[5], vp[6],
+                                   ctypes.c_void_p(FAKE), 1 << 40, None)
+        assert rc == 1 and "dropout" in L.df_last_error().decode()
+    p15 = [ctypes.c_void_p(FAKE)] * 15
+    rc = L.df_attn_bwd_dropout(ctypes.byref(s), *p15[:5], 512, 256, None, None, 1.5, 1, 0, *p15[5:13],
+                               ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert rc == 1 and "dropout" in L.df_last_error().decode()
+    rc = L.df_attn_fwd_dropout(ctypes.byref(s), *vp[:5], 512, 256, None, None, 0.1, 1, 0, vp[5], None,
+                               ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert rc == 1
+
+
 def test_bwd_and_index_reject_on_host(df):
     L = df.lib()
     s = _shape(df)

@@ -116,3 +116,45 @@ def test_inference_forward(name):
     ref = run_oracle(inp, backward=False)
     err = rel_l2(out_i.float().cpu().numpy(), ref["out"])
     assert np.isfinite(err) and err <= TOL[inp.dtype][0], err
+
+
+# ----------------------------------------------------------------------------
+# attention-probability dropout: the kernels regenerate the oracle's Philox
+# mask (both sides implement the generator from its definition)
+
+DROP_CASES = {
+    "bf16_D64_bucketed_ragged": (0.1, 1234, 5),
+    "fp32_D64": (0.3, 0xDEADBEEF12345, 0),
+    "bf16_packed_masked": (0.2, 77, 9),
+    "fp16_D128_unbucketed": (0.15, 3, 1),
+    "tiny_fp32_L64": (0.5, 1, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(DROP_CASES))
+def test_dropout_parity(name):
+    import deberta_disentangled_attention_rel_amd as df
+    from parity_util import to_dev, rel_l2, TOL
+    print(f"dropout {name}", flush=True)
+    p, seed, offset = DROP_CASES[name]
+    inp = _inp(**CASES[name])
+    w = inp.workload
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    dkw = dict(dropout_p=p, seed=seed, offset=offset)
+    out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw, **dkw)
+    g = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out, lse, t["dout"], **kw, **dkw)
+    torch.cuda.synchronize()
+    f = inp.f64
+    okw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq, dropout=(p, seed, offset))
+    ref_o, ref_l = oracle.forward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], w.span, w.buckets, **okw)
+    ref_g = oracle.backward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], f["dout"], w.span, w.buckets, **okw)
+    tol_f, tol_b = TOL[inp.dtype]
+    errs = {"out": rel_l2(out.float().cpu().numpy(), ref_o)}
+    valid = np.isfinite(ref_l)
+    errs["lse"] = rel_l2(lse.cpu().numpy()[valid], ref_l[valid])
+    for n_, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g, ref_g):
+        errs[n_] = rel_l2(a.float().cpu().numpy(), b)
+    bad = {n_: e for n_, e in errs.items()
+           if not np.isfinite(e) or e > (tol_f if n_ in ("out", "lse") else tol_b)}
+    assert not bad, (errs, bad)

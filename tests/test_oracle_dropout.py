@@ -70,6 +70,7 @@ def test_keep_fraction_and_stream_separation():
         agree = (other == m).mean()
         assert abs(agree - (p * p + (1 - p) * (1 - p))) <= 0.02
     assert philox.keep_mask(0.0, 42, 0, 0, 0, H, L).all()
+    assert philox.keep_mask(p, 42, 0, 0, 0, H, 0).shape == (0, 0)  # empty sequence
     with pytest.raises(ValueError):
         philox.keep_threshold(1.0)
 
