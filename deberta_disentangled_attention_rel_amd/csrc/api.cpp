@@ -90,12 +90,22 @@ int check_all(const df_attn_shape* s, int32_t span, int32_t buckets, bool packed
   if (!packed && int64_t(s->batch) * s->max_seqlen != s->total_tokens)
     return fail(DF_ERR_INVALID, "padded layout needs total_tokens == batch*max_seqlen (%lld != %d*%d)",
                 (long long)s->total_tokens, s->batch, s->max_seqlen);
+  {
+    // the kernels address one sequence's rows of one head (and its strip
+    // rows) with 32-bit byte offsets through buffer views
+    const int64_t es = int64_t(dtype_size(s->dtype)), rp = (int64_t(*R) + 7) / 8 * 8;
+    const int64_t row = s->tok_stride > rp ? s->tok_stride : rp;
+    if (int64_t(s->max_seqlen) * row * es >= (int64_t(1) << 31))
+      return fail(DF_ERR_UNSUPPORTED,
+                  "one sequence's rows of a head must span less than 2 GiB (max_seqlen %d x row %lld elements)",
+                  s->max_seqlen, (long long)row);
+  }
   return DF_OK;
 }
 
 // Workspace plan. Offsets are relative to the workspace base.
 struct Plan {
-  size_t lut, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
+  size_t lut, lutp, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
   int RP, nchunk, chunk_tokens;
 };
 
@@ -111,6 +121,7 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
     return at;
   };
   pl.lut = take(2 * (2 * size_t(s->max_seqlen) - 1) * sizeof(int32_t));
+  pl.lutp = take((2 * size_t(s->max_seqlen) - 1 + 2 * dfa::kLutPad) * sizeof(uint32_t));
   pl.c2ps = take(H * T * pl.RP * es);
   pl.p2cs = take(H * T * pl.RP * es);
   pl.ends = take(4 * H * T * es);
@@ -194,6 +205,7 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
   p.scale_log2 = float(1.4426950408889634 / std::sqrt(3.0 * s->head_dim));
   p.c2p = reinterpret_cast<int32_t*>(ws + pl.lut);
   p.p2c = p.c2p + (2 * size_t(s->max_seqlen) - 1);
+  p.lutp = reinterpret_cast<const uint32_t*>(ws + pl.lutp);
   // narrow kernels keep both rows of a table entry as 16-bit byte offsets
   const size_t esize = s->dtype == DF_FP32 ? 4 : 2;
   p.narrow = (narrow_tables(span, buckets) && size_t(R - 1) * esize <= 0xffff) ? 1 : 0;
@@ -321,7 +333,7 @@ int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets, int32_
   int rc = index_params(span, buckets, &att, &R);
   if (rc) return rc;
   if (!c2p_lut || !p2c_lut) return fail(DF_ERR_INVALID, "table pointers must not be NULL");
-  rc = hip_check(dfa::launch_lut(max_seqlen, span, buckets, c2p_lut, p2c_lut, (hipStream_t)stream),
+  rc = hip_check(dfa::launch_lut(max_seqlen, span, buckets, c2p_lut, p2c_lut, nullptr, (hipStream_t)stream),
                  "relative index kernel");
   return rc ? rc : ok();
 }
@@ -378,7 +390,7 @@ int fwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                     [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+                     [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, const_cast<uint32_t*>(p.lutp), st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
     return rc;
@@ -454,7 +466,7 @@ int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                       [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, st); })) ||
+                       [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, const_cast<uint32_t*>(p.lutp), st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
         (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||

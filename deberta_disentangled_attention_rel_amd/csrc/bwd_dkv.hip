@@ -107,43 +107,62 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   QTile qt, ot;
   qt.init();
   ot.init();
-  float ureg = 0.f, dreg = 0.f;
-  uint32_t lreg = 0;
+  // buffer views of this sequence's rows (reads past its end return zero)
+  // and this thread's fixed offsets into them, so that issuing a query tile
+  // takes no address arithmetic
+  const uint32_t seq_bytes = uint32_t(sq.len) * uint32_t(p.ts * ES);
+  const BufView qview = buf_view(qbase, seq_bytes), oview = buf_view(dobase, seq_bytes);
+  [[maybe_unused]] DmaRows<T, BM, D, QP, 256, true> qdma;  // half-major, the same offsets for Q and dO
+  if constexpr (DMA) qdma.init(p.ts);
+  const BufView lview = buf_view(p.lutp, uint32_t(2 * p.Lmax - 1 + 2 * kLutPad) * 4u);
+  // table slice entry tid of query tile qb is packed entry (qb*BM - j0 - BN + 1 + tid) + Lmax - 1 + kLutPad
+  const int lvoff = (tid - j0 - BN + 1 + p.Lmax - 1 + kLutPad) * 4;
+  const BufView mview = buf_view(kmask, kmask ? uint32_t(sq.len) : 0u);
+  const BufView lsev = buf_view(lse, uint32_t(sq.len) * 4u), dltv = buf_view(dlt, uint32_t(sq.len) * 4u);
+  const BufView eview_l = buf_view(ends + c2p_end_of(TILE_FAR_LEFT) * HT + sq.start, uint32_t(sq.len) * ES);
+  const BufView eview_r = buf_view(ends + c2p_end_of(TILE_FAR_RIGHT) * HT + sq.start, uint32_t(sq.len) * ES);
+  // the next tile's per-query values and table slice, loaded raw and only
+  // used when the tile is committed
+  T a_raw = TR::from_f(0.f);
+  float lse_raw = 0.f, dlt_raw = 0.f;
+  uint32_t m_raw = 1u, lreg = 0;
 
   auto prefetch = [&](int qb) {
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
     if constexpr (DMA) {
       // straight into the free LDS buffer (last read two tiles ago)
-      DmaTile<T, BM, D, QP, 256, true>::issue(Qs[qb & 1], qbase, p.ts, i0, sq.len);
-      DmaTile<T, BM, D, QP, 256, true>::issue(dOs[qb & 1], dobase, p.ts, i0, sq.len);
+      qdma.issue(Qs[qb & 1], qview, i0 * int(p.ts) * ES);
+      qdma.issue(dOs[qb & 1], oview, i0 * int(p.ts) * ES);
     } else {
       qt.load(qbase, p.ts, i0, sq.len);
       ot.load(dobase, p.ts, i0, sq.len);
     }
     if (tid < BM) {
-      const int i = i0 + tid;
-      const bool in = i < sq.len;
-      const int ic = in ? i : sq.len - 1;
-      const bool ok = in && (!kmask || kmask[ic]);
-      float a = 0.f;
-      if (cls != TILE_BAND) a = TR::to_f(ends[c2p_end_of(cls) * HT + sq.start + ic]);
-      ureg = ok ? a - lse[ic] * kLog2e : -INFINITY;
-      dreg = ok ? dlt[ic] : 0.f;
+      // past the sequence end all of these read 0 (the row is masked there)
+      if (kmask) m_raw = buf_load_u8(mview, i0 + tid);
+      a_raw = buf_load<T>(cls == TILE_FAR_LEFT ? eview_l : eview_r, tid * ES, i0 * ES);
+      lse_raw = buf_load<float>(lsev, tid * 4, i0 * 4);
+      dlt_raw = buf_load<float>(dltv, tid * 4, i0 * 4);
     }
-    if (cls == TILE_BAND && tid < NL)
-      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
+    if (cls == TILE_BAND && tid < NL) lreg = buf_load<uint32_t>(lview, lvoff + i0 * 4, 0);
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](int qb) {
+    const int buf = qb & 1;
+    const int i0 = qb * BM;
+    const int cls = cls_of(qb);
     if constexpr (!DMA) {
       qt.template store<QP>(Qs[buf]);
       ot.template store<QP>(dOs[buf]);
     }
     if (tid < BM) {
-      uq_s[buf][tid] = ureg;
-      dlt_s[buf][tid] = dreg;
+      const bool ok = i0 + tid < sq.len && m_raw != 0u;
+      const float a = cls != TILE_BAND ? TR::to_f(a_raw) : 0.f;
+      uq_s[buf][tid] = ok ? a - lse_raw * kLog2e : -INFINITY;
+      dlt_s[buf][tid] = ok ? dlt_raw : 0.f;
     }
-    if (tid < NL) lut_s[buf][tid] = lreg;
+    // both 16-bit halves scale to byte offsets at once (narrow: (R-1)*ES fits 16 bits)
+    if (tid < NL) lut_s[buf][tid] = NARROW ? lreg * ES : lreg;
   };
 
   f32x16 dVt[ND], dKt[ND];
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           // this tile's last gather is issued: publish the next tile's table
           // slice, wait for every wave to be done with the windows, then copy
           // the next tile's windows while this tile finishes
-          if (tid < NL) lut_s[buf ^ 1][tid] = lreg;
+          if (tid < NL) lut_s[buf ^ 1][tid] = NARROW ? lreg * ES : lreg;
           __syncthreads();
           issue_windows(buf ^ 1, i0 + BM);
         }
@@ -316,7 +335,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     } else {
       walk_merge<TR>(wrow, R, g, wk, rc, sc, jin);
     }
-    if (qb + 1 < nqb) commit(buf ^ 1);
+    if (qb + 1 < nqb) commit(qb + 1);
     wait_vmem();
     __syncthreads();
   }

@@ -102,15 +102,34 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     return tile_class(i0 - j0 - BN + 1, i0 + BM - 1 - j0, d_hi, d_lo);
   };
 
+  // buffer views of this sequence's rows (reads past its end return zero)
+  // and this thread's fixed offsets into them: issuing a tile's loads then
+  // needs no address arithmetic
+  const uint32_t seq_bytes = uint32_t(sq.len) * uint32_t(p.ts * ES);
+  const BufView kview = buf_view(kbase, seq_bytes), vview = buf_view(vbase, seq_bytes);
+  [[maybe_unused]] DmaRows<T, BN, D, KP, 256> kdma;
+  [[maybe_unused]] DmaRows<T, BN, D, VP, 256> vdma;
+  if constexpr (DMA) {
+    kdma.init(p.ts);
+    vdma.init(p.ts);
+  }
+  const BufView lview = buf_view(p.lutp, uint32_t(2 * p.Lmax - 1 + 2 * kLutPad) * 4u);
+  // table slice entry tid of tile kb is packed entry (i0 - kb*BN - BN + 1 + tid) + Lmax - 1 + kLutPad
+  const int lvoff = (i0 - BN + 1 + tid + p.Lmax - 1 + kLutPad) * 4;
+  const BufView mview = buf_view(kmask, kmask ? uint32_t(sq.len) : 0u);
+  const BufView eview_l = buf_view(ends + p2c_end_of(TILE_FAR_LEFT) * HT + sq.start, uint32_t(sq.len) * ES);
+  const BufView eview_r = buf_view(ends + p2c_end_of(TILE_FAR_RIGHT) * HT + sq.start, uint32_t(sq.len) * ES);
+
   // ---- next-tile registers
   KTile kt, vt;
   kt.init();
   vt.init();
   // the next tile's per-key values and table slice, loaded raw and only
   // used when the tile is committed, so nothing waits for them (or for the
-  // tile copy issued after them) before then
+  // tile copy issued after them) before then; key mask and end values past
+  // the sequence read 0 (the key is masked there anyway)
   T e_raw = TR::from_f(0.f);
-  uint32_t m_raw = 1u, c_raw = 0u, p_raw = 0u;
+  uint32_t m_raw = 1u, l_raw = 0u;
 
   // Issue the loads of tile kb into buffer Q (free since the last barrier).
   auto prefetch = [&](int kb, auto q_c) {
@@ -118,19 +137,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
     if (tid < BN) {
-      const int jc = min(j0 + tid, sq.len - 1);
-      m_raw = kmask ? kmask[jc] : 1u;
-      e_raw = ends[p2c_end_of(cls == TILE_BAND ? TILE_FAR_LEFT : cls) * HT + sq.start + jc];
+      if (kmask) m_raw = buf_load_u8(mview, j0 + tid);
+      e_raw = buf_load<T>(cls == TILE_FAR_LEFT ? eview_l : eview_r, tid * ES, j0 * ES);
     }
-    if (tid < NL) {
-      const int off = p.Lmax - 1, d = i0 - j0 - BN + 1 + tid;
-      const int n = d < -off ? 0 : (d > off ? 2 * off : d + off);
-      c_raw = uint32_t(p.c2p[n]);
-      p_raw = uint32_t(p.p2c[n]);
-    }
+    if (tid < NL) l_raw = buf_load<uint32_t>(lview, lvoff - j0 * 4, 0);
     if constexpr (DMA) {
-      DmaTile<T, BN, D, KP, 256>::issue(Q ? Ks1 : Ks0, kbase, p.ts, j0, sq.len);
-      DmaTile<T, BN, D, VP, 256>::issue(Q ? Vs1 : Vs0, vbase, p.ts, j0, sq.len);
+      kdma.issue(Q ? Ks1 : Ks0, kview, j0 * int(p.ts) * ES);
+      vdma.issue(Q ? Vs1 : Vs0, vview, j0 * int(p.ts) * ES);
     } else {
       kt.load(kbase, p.ts, j0, sq.len);
       vt.load(vbase, p.ts, j0, sq.len);
@@ -149,7 +162,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       const bool ok = j0 + tid < sq.len && m_raw != 0u;
       bj_s[Q][tid] = ok ? (cls != TILE_BAND ? TR::to_f(e_raw) : 0.f) : -INFINITY;
     }
-    if (tid < NL) lut_s[Q][tid] = NARROW ? (c_raw * ES | (p_raw * ES) << 16) : (c_raw | p_raw << 16);
+    // both 16-bit halves scale to byte offsets at once (narrow: (R-1)*ES fits 16 bits)
+    if (tid < NL) lut_s[Q][tid] = NARROW ? l_raw * ES : l_raw;
   };
 
   f32x16 O[ND];

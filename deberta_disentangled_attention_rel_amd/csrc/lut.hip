@@ -77,25 +77,36 @@ __device__ int bucket_of(int d, int span, int buckets) {
 }
 
 __global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict__ c2p,
-                           int32_t* __restrict__ p2c) {
+                           int32_t* __restrict__ p2c, uint32_t* __restrict__ packed) {
+  // with `packed`, thread n also writes entry n of the padded packed table
+  // (kLutPad entries on each side repeat the end entries)
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= 2 * Lmax - 1) return;
-  const int d = n - (Lmax - 1);
+  const int pad = packed ? kLutPad : 0;
+  if (n >= 2 * Lmax - 1 + 2 * pad) return;
+  int d = n - pad - (Lmax - 1);
+  d = d < -(Lmax - 1) ? -(Lmax - 1) : (d > Lmax - 1 ? Lmax - 1 : d);
   const int att = buckets > 0 ? buckets : span;
   const int R = 2 * att;
   // bucket is odd, so the P2C row needs no second evaluation
   const int b = bucket_of(d, span, buckets);
   int c = b + att;
   int p = att - b;
-  c2p[n] = c < 0 ? 0 : (c > R - 1 ? R - 1 : c);
-  p2c[n] = p < 0 ? 0 : (p > R - 1 ? R - 1 : p);
+  c = c < 0 ? 0 : (c > R - 1 ? R - 1 : c);
+  p = p < 0 ? 0 : (p > R - 1 ? R - 1 : p);
+  const int m = n - pad;
+  if (m >= 0 && m < 2 * Lmax - 1) {
+    c2p[m] = c;
+    p2c[m] = p;
+  }
+  if (packed) packed[n] = uint32_t(c) | (uint32_t(p) << 16);
 }
 
 }  // namespace
 
-hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st) {
-  const int n = 2 * Lmax - 1;
-  lut_kernel<<<(n + 255) / 256, 256, 0, st>>>(Lmax, span, buckets, c2p, p2c);
+hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, uint32_t* packed,
+                      hipStream_t st) {
+  const int n = 2 * Lmax - 1 + (packed ? 2 * kLutPad : 0);
+  lut_kernel<<<(n + 255) / 256, 256, 0, st>>>(Lmax, span, buckets, c2p, p2c, packed);
   return hipGetLastError();
 }
 

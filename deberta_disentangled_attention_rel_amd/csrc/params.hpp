@@ -9,6 +9,10 @@ namespace dfa {
 
 constexpr int DF_BF16_T = 0, DF_FP16_T = 1, DF_FP32_T = 2;
 
+// Entries on each side of the padded packed index table (at least the
+// largest tile edge, so a tile's table slice never needs a clamp).
+constexpr int kLutPad = 256;
+
 // Everything a kernel of the path may need. Pointers are device pointers.
 struct Params {
   // shape
@@ -23,6 +27,9 @@ struct Params {
   // relative index tables, entry d + Lmax - 1
   int32_t* c2p;
   int32_t* p2c;
+  // the same tables packed (c2p | p2c << 16), entry d + Lmax - 1 + kLutPad, with
+  // kLutPad copies of the end entries on each side: [2 Lmax - 1 + 2 kLutPad]
+  const uint32_t* lutp;
   int d_hi, d_lo;           // far field: both tables at their end rows iff d >= d_hi or d <= d_lo
   int narrow;               // 1 if neither table ever steps by more than one row
   // user tensors
@@ -52,7 +59,8 @@ struct Params {
 };
 
 // launchers (each returns hipGetLastError() after its launches)
-hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, hipStream_t st);
+hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, uint32_t* packed,
+                      hipStream_t st);  // packed may be null
 hipError_t launch_strips(const Params& p, hipStream_t st);  // both strips
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);

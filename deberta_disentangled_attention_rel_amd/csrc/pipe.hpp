@@ -235,6 +235,48 @@ struct DmaTile {
   }
 };
 
+// The same copy through a buffer view of one sequence's rows of one head
+// (`bytes` = rows x token stride x element size): each thread's byte offsets
+// within a tile are fixed (init), the tile's first row enters as a scalar
+// offset, so issuing a tile takes no address arithmetic. Rows at or past the
+// end of the view, and the row-padding chunks, load zeros without touching
+// memory (the hardware range check).
+template <typename T, int ROWS, int D, int P, int NT, bool HALF_MAJOR = false>
+struct DmaRows {
+  static constexpr int PC = P / 8, NC = D / 8;
+  static constexpr int SLOTS = ROWS * PC;
+  static constexpr int NI = (SLOTS + NT - 1) / NT;
+  int voff[NI];
+
+  __device__ __forceinline__ void init(int64_t ts) {
+    static_assert(sizeof(T) == 2 && P % 8 == 0 && D % 8 == 0, "16-bit rows of whole 16-byte chunks");
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int s = k * NT + int(threadIdx.x);
+      const int slot = s / PC, c = s % PC;
+      const int row = HALF_MAJOR ? half_major_at<ROWS / 32>(slot) : slot;
+      voff[k] = (s < SLOTS && c < NC) ? int(row * ts * int64_t(sizeof(T))) + c * 16 : kBufSkip;
+    }
+  }
+  // rows row0 .. row0 + ROWS - 1 of the view, row0 * ts * sizeof(T) = soff
+  __device__ __forceinline__ void issue(T* lds, BufView b, int soff) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int s0 = k * NT + wave * 64;
+      if (s0 >= SLOTS) break;  // wave-uniform
+      if (k * NT + int(threadIdx.x) < SLOTS) {
+        // device pass only: in the host pass this builtin inside the kernels'
+        // lambdas silently drops the kernels' launch stubs
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16,
+                                                 voff[k], soff, 0, 0);
+#endif
+      }
+    }
+  }
+};
+
 // Wait for this thread's outstanding vector-memory loads, LDS-DMA included
 // (vmcnt(0); export and LDS counters left alone).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

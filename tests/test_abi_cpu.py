@@ -80,9 +80,10 @@ def test_workspace_sizes(df):
     s = _shape(df)
     w0, w1 = df.workspace_size(0, s, 512, 256), df.workspace_size(1, s, 512, 256)
     assert 0 < w0 < w1
-    # forward: two tables + two strips [H][T][R] + four end columns, 256-byte aligned pieces
+    # forward: two tables, the packed table with 256 entries of padding on each
+    # side, two strips [H][T][R] and four end columns, 256-byte aligned pieces
     T, H, R, L = 256, 4, 512, 128
-    expect = [2 * (2 * L - 1) * 4, H * T * R * 2, H * T * R * 2, 4 * H * T * 2]
+    expect = [2 * (2 * L - 1) * 4, (2 * L - 1 + 2 * 256) * 4, H * T * R * 2, H * T * R * 2, 4 * H * T * 2]
     assert w0 == sum((x + 255) // 256 * 256 for x in expect)
     assert df.workspace_size(2, s, 512, 256) == 0
     assert df.workspace_size(0, _shape(df, head_dim=48), 512, 256) == 0
