@@ -94,32 +94,46 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   KTile kt, vt;
   kt.init();
   vt.init();
-  float breg = 0.f;
-  uint32_t lreg = 0;
+  // buffer views of this sequence's rows (reads past its end return zero),
+  // so that a tile's loads take a scalar row offset and no branch
+  const uint32_t seq_bytes = uint32_t(sq.len) * uint32_t(p.ts * ES);
+  const BufView kview = buf_view(kbase, seq_bytes), vview = buf_view(vbase, seq_bytes);
+  const BufView lview = buf_view(p.lutp, uint32_t(2 * p.Lmax - 1 + 2 * kLutPad) * 4u);
+  // table slice entry tid of key tile kb is packed entry (i0 - kb*BN - BN + 1 + tid) + Lmax - 1 + kLutPad
+  const int lvoff = (i0 - BN + 1 + tid + p.Lmax - 1 + kLutPad) * 4;
+  const BufView mview = buf_view(kmask, kmask ? uint32_t(sq.len) : 0u);
+  const BufView eview_l = buf_view(ends + p2c_end_of(TILE_FAR_LEFT) * HT + sq.start, uint32_t(sq.len) * ES);
+  const BufView eview_r = buf_view(ends + p2c_end_of(TILE_FAR_RIGHT) * HT + sq.start, uint32_t(sq.len) * ES);
+  // the next tile's per-key values and table slice, loaded raw and used when
+  // the tile is committed (past the sequence end they read 0; such keys are
+  // masked)
+  T e_raw = TR::from_f(0.f);
+  uint32_t m_raw = 1u, lreg = 0;
 
   auto prefetch = [&](int kb) {
     const int j0 = kb * BN;
     const int cls = cls_of(kb);
-    kt.load(kbase, p.ts, j0, sq.len);
-    vt.load(vbase, p.ts, j0, sq.len);
+    kt.load_buf(kview, p.ts, j0 * int(p.ts) * ES);
+    vt.load_buf(vview, p.ts, j0 * int(p.ts) * ES);
     if (tid < BN) {
-      const int j = j0 + tid;
-      const bool in = j < sq.len;
-      const int jc = in ? j : sq.len - 1;
-      const bool ok = in && (!kmask || kmask[jc]);
-      float b = 0.f;
-      if (cls != TILE_BAND) b = TR::to_f(ends[p2c_end_of(cls) * HT + sq.start + jc]);
-      breg = ok ? b : -INFINITY;
+      if (kmask) m_raw = buf_load_u8(mview, j0 + tid);
+      e_raw = buf_load<T>(cls == TILE_FAR_LEFT ? eview_l : eview_r, tid * ES, j0 * ES);
     }
-    if (cls == TILE_BAND && tid < NL)
-      lreg = NARROW ? lut_entry_bytes<ES>(p, i0 - j0 - BN + 1 + tid) : lut_entry(p, i0 - j0 - BN + 1 + tid);
+    if (cls == TILE_BAND && tid < NL) lreg = buf_load<uint32_t>(lview, lvoff - j0 * 4, 0);
   };
 
-  auto commit = [&](int buf) {
+  auto commit = [&](int kb) {
+    const int buf = kb & 1;
+    const int j0 = kb * BN;
+    const int cls = cls_of(kb);
     kt.template store<KP>(Ks[buf]);
     vt.template store<KP>(Vs[buf]);
-    if (tid < BN) bj_s[buf][tid] = breg;
-    if (tid < NL) lut_s[buf][tid] = lreg;
+    if (tid < BN) {
+      const bool ok = j0 + tid < sq.len && m_raw != 0u;
+      bj_s[buf][tid] = ok ? (cls != TILE_BAND ? TR::to_f(e_raw) : 0.f) : -INFINITY;
+    }
+    // both 16-bit halves scale to byte offsets at once (narrow: (R-1)*ES fits 16 bits)
+    if (tid < NL) lut_s[buf][tid] = NARROW ? lreg * ES : lreg;
   };
 
   f32x16 dQt[ND];
@@ -280,7 +294,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     else
       body(BoolC<false>{});
 
-    if (kb + 1 < nkb) commit(buf ^ 1);
+    if (kb + 1 < nkb) commit(kb + 1);
     __syncthreads();
   }
 

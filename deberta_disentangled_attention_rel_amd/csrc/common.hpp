@@ -192,8 +192,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buf_store16(BufView b, int voff, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, b.r, voff, 0, 0);
 }
-__device__ __forceinline__ uint4 buf_load16(BufView b, int voff) {
-  const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, 0, 0);
+__device__ __forceinline__ uint4 buf_load16(BufView b, int voff, int soff = 0) {
+  const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, soff, 0);
   return make_uint4(r.x, r.y, r.z, r.w);
 }
 

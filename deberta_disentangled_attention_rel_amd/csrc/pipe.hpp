@@ -125,6 +125,17 @@ struct RowTile {
         r[u] = *reinterpret_cast<const uint4*>(base + int64_t(row0 + row) * ts + col_of(u));
     }
   }
+  // the same rows through a buffer view of the sequence's rows (token stride
+  // ts elements): row0 * ts * sizeof(T) = soff; rows past the view load zero
+  // with no branch
+  __device__ __forceinline__ void load_buf(BufView b, int64_t ts, int soff) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int row = row_of(u);
+      const int voff = row < ROWS ? int(row * ts * int64_t(sizeof(T))) + col_of(u) * int(sizeof(T)) : kBufSkip;
+      r[u] = buf_load16(b, voff, soff);
+    }
+  }
   template <int P>
   __device__ __forceinline__ void store(T* __restrict__ lds) const {
 #pragma unroll
