@@ -10,3 +10,4 @@ from .df_oracle import (  # noqa: F401
     forward, backward, forward_rows, dq_rows,
 )
 from . import philox  # noqa: F401
+from .proj import qkv_projection  # noqa: F401
