@@ -219,6 +219,17 @@ def main(argv=None) -> int:
     drop_step()
     drop_ms = timed(drop_step, max(1, a.steps // 3))
 
+    # the fused Q/K/V + relative projections that produce this workload's
+    # inputs (hidden size H*D, relative rows R), timed on their own: not part
+    # of the page's FLOP convention or of the step
+    from synth import make_proj_inputs
+    pin = make_proj_inputs(B * L, H * D, H, D, R, "bf16", seed=77)
+    pt = {k_: v_.to(dev) for k_, v_ in pin.t.items()}
+    pouts = df.qkv_proj(pt["x"], pt["w"], pt["bias"], pt["rel"], H, D)
+    proj_ms = timed(lambda: df.qkv_proj(pt["x"], pt["w"], pt["bias"], pt["rel"], H, D, out=pouts), a.steps)
+    proj_flops = 2.0 * B * L * (H * D) * 3 * H * D + 2.0 * R * (H * D) * 2 * H * D
+    del pt, pouts
+
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
     tflops = fl / (ms * 1e-3) / 1e12
@@ -260,6 +271,8 @@ def main(argv=None) -> int:
         "bwd_ms": round(bwd_ms, 4),
         "inference_fwd_ms": round(inf_ms, 4),
         "dropout_0.1_step_ms": round(drop_ms, 4),
+        "qkv_proj": {"ms": round(proj_ms, 4), "tflops": round(proj_flops / (proj_ms * 1e-3) / 1e12, 1),
+                     "shape": f"x [{B * L}, {H * D}] w [{3 * H * D}, {H * D}] rel [{R}, {H * D}]"},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),

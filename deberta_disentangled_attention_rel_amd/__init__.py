@@ -18,6 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "fwd_inference", "bwd",
+           "qkv_proj",
            "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
@@ -27,7 +28,7 @@ EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
             "df_attn_fwd", "df_attn_fwd_inference", "df_attn_bwd", "df_attn_fwd_dropout",
             "df_attn_bwd_dropout", "df_strerror", "df_last_error",
             "df_attn_version",
-            "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name")
+            "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name", "df_qkv_proj")
 NUM_STAGES = 9
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.df_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, vp, vp, sz, vp]
     L.df_attn_bwd.restype = ctypes.c_int
+    L.df_qkv_proj.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.df_qkv_proj.restype = ctypes.c_int
     L.df_strerror.argtypes = [ctypes.c_int]
     L.df_strerror.restype = ctypes.c_char_p
     L.df_last_error.argtypes = []
@@ -269,3 +272,33 @@ def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=Non
     if q.dim() == 4:
         dq, dk, dv = (x.view(q.shape) for x in (dq, dk, dv))
     return dq, dk, dv, dq_r, dk_r
+
+
+def qkv_proj(x, w, bias, rel, num_heads: int, head_dim: int, out=None):
+    """Fused Q/K/V and relative-position projections (``df_qkv_proj``).
+
+    ``x`` [T, E], ``w`` [3*H*D, E] (rows W_q, W_k, W_v), ``bias`` [3*H*D] or
+    None, ``rel`` [R, E] or None. Returns ``(q, k, v, q_r, k_r)``: q, k, v
+    contiguous [T, H, D], q_r, k_r [H, R, D] (None without ``rel``)."""
+    H, D = int(num_heads), int(head_dim)
+    T, E = x.shape
+    if w.shape != (3 * H * D, E) or w.dtype != x.dtype or (bias is not None and bias.shape != (3 * H * D,)):
+        raise ValueError("w must be [3*H*D, E] and bias [3*H*D], in x's dtype")
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("df_qkv_proj takes bf16 or fp16")
+    x, w = x.contiguous(), w.contiguous()
+    bias = bias.contiguous() if bias is not None else None
+    R = 0 if rel is None else rel.shape[0]
+    if rel is not None:
+        if rel.shape[1] != E or rel.dtype != x.dtype:
+            raise ValueError("rel must be [R, E] in x's dtype")
+        rel = rel.contiguous()
+    if out is None:
+        q, k, v = (torch.empty((T, H, D), dtype=x.dtype, device=x.device) for _ in range(3))
+        q_r, k_r = ((torch.empty((H, R, D), dtype=x.dtype, device=x.device) for _ in range(2))
+                    if rel is not None else (None, None))
+    else:
+        q, k, v, q_r, k_r = out
+    _check(lib().df_qkv_proj(T, E, H, D, R, DTYPE_CODES[x.dtype], _ptr(x), _ptr(w), _ptr(bias), _ptr(rel),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(q_r), _ptr(k_r), _stream(x.device)))
+    return q, k, v, q_r, k_r

@@ -520,3 +520,73 @@ int df_attn_bwd_dropout(const df_attn_shape* shape, const void* q, const void* k
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Fused Q/K/V and relative-position projections.
+
+extern "C" {
+
+int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim, int32_t rel_rows,
+                int32_t dtype, const void* x, const void* w, const void* bias, const void* rel, void* q, void* k,
+                void* v, void* q_r, void* k_r, void* stream) {
+  if (dtype == DF_FP32)
+    return fail(DF_ERR_UNSUPPORTED, "df_qkv_proj takes 16-bit operands (bf16 or fp16), not fp32");
+  if (dtype != DF_BF16 && dtype != DF_FP16) return fail(DF_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(DF_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128, got %d", head_dim);
+  if (num_heads < 1 || num_heads > 65535)
+    return fail(DF_ERR_INVALID, "num_heads must be in [1, 65535], got %d", num_heads);
+  if (hidden < 8 || hidden % 8)
+    return fail(DF_ERR_INVALID, "hidden must be a positive multiple of 8, got %d", hidden);
+  if (tokens < 0) return fail(DF_ERR_INVALID, "tokens must be >= 0");
+  if (rel_rows < 0) return fail(DF_ERR_INVALID, "rel_rows must be >= 0");
+  const int64_t HD = int64_t(num_heads) * head_dim;
+  // operand rows are addressed with 32-bit byte offsets per 128-row block
+  if (int64_t(hidden) * 2 * 128 >= (int64_t(1) << 31) || 3 * HD >= (int64_t(1) << 31) ||
+      tokens * HD >= (int64_t(1) << 40))
+    return fail(DF_ERR_UNSUPPORTED, "projection too large (tokens %lld, hidden %d, heads x dim %lld)",
+                (long long)tokens, hidden, (long long)HD);
+  int rc;
+  if ((rc = check_ptr(w, "w", 16)) || (tokens > 0 && (rc = check_ptr(x, "x", 16))) ||
+      (tokens > 0 && ((rc = check_ptr(q, "q", 2)) || (rc = check_ptr(k, "k", 2)) || (rc = check_ptr(v, "v", 2)))))
+    return rc;
+  if (bias && !aligned(bias, 2)) return fail(DF_ERR_INVALID, "bias must be 2-byte aligned");
+  const bool want_rel = rel != nullptr && rel_rows > 0;
+  if (want_rel && ((rc = check_ptr(rel, "rel", 16)) || (rc = check_ptr(q_r, "q_r", 2)) ||
+                   (rc = check_ptr(k_r, "k_r", 2))))
+    return rc;
+  if (!rel && rel_rows > 0) return fail(DF_ERR_INVALID, "rel is NULL but rel_rows = %d", rel_rows);
+  const hipStream_t st = (hipStream_t)stream;
+  dfa::ProjParams p{};
+  p.w = w;
+  p.bias = bias;
+  p.K = hidden;
+  p.HD = int(HD);
+  p.D = head_dim;
+  p.R = rel_rows;
+  p.dtype = dtype;
+  if (tokens > 0) {
+    p.a = x;
+    p.M = int(tokens);
+    p.N = int(3 * HD);
+    p.mode = 0;
+    p.out0 = q;
+    p.out1 = k;
+    p.out2 = v;
+    if (tokens > (int64_t(1) << 31) - 1) return fail(DF_ERR_UNSUPPORTED, "tokens must be < 2^31");
+    if ((rc = hip_check(dfa::launch_proj(p, st), "projection (tokens)"))) return rc;
+  }
+  if (want_rel) {
+    p.a = rel;
+    p.M = rel_rows;
+    p.N = int(2 * HD);
+    p.mode = 1;
+    p.out0 = q_r;
+    p.out1 = k_r;
+    p.out2 = nullptr;
+    if ((rc = hip_check(dfa::launch_proj(p, st), "projection (relative rows)"))) return rc;
+  }
+  return ok();
+}
+
+}  // extern "C"

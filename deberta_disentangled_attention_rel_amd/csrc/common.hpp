@@ -156,8 +156,10 @@ __device__ __forceinline__ float xor32(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer view of `bytes` bytes at `base`: loads at offsets past the end
-// return zero (the hardware range check), so a gather may run past the end
-// of a sequence without touching memory there.
+// return zero (the hardware range check, which on gfx950 covers the per-lane
+// offset, the scalar offset and their sum; checked with an in-bounds probe),
+// so a gather may run past the end of a sequence without touching memory
+// there.
 struct BufView {
   __amdgpu_buffer_rsrc_t r;
 };

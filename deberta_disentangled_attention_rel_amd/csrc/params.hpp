@@ -58,6 +58,21 @@ struct Params {
   int chunk_tokens;
 };
 
+// One projection GEMM Y = A W^T + bias (16-bit operands, fp32 accumulation):
+// A [M, K], W rows [N, K] (both K-contiguous), bias [N] or null. mode 0:
+// column n = which * HD + hd goes to out<which>[m * HD + hd] ([T, H, D]);
+// mode 1: to out<which>[(hd / D) * R + m) * D + hd % D] ([H, R, D]).
+struct ProjParams {
+  const void* a;
+  const void* w;
+  const void* bias;
+  int M, N, K;
+  int HD, D, R;
+  int mode;
+  int dtype;
+  void *out0, *out1, *out2;
+};
+
 // launchers (each returns hipGetLastError() after its launches)
 hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, uint32_t* packed,
                       hipStream_t st);  // packed may be null
@@ -69,5 +84,6 @@ hipError_t launch_bwd_dq(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_dx(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_dw(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_sum(const Params& p, hipStream_t st);
+hipError_t launch_proj(const ProjParams& p, hipStream_t st);
 
 }  // namespace dfa

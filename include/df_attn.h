@@ -169,6 +169,32 @@ int df_attn_bwd_dropout(const df_attn_shape* shape,
                         void* dq, void* dk, void* dv, void* dq_r, void* dk_r,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+
+/* Fused Q/K/V and relative-position projections (DisentangledFlash 1.1.1
+ * page, "Status": the fused QKV projection is always enabled; "Hugging Face
+ * usage": the Q/K/V and relative-position projections stay in the model's
+ * graph). One GEMM with the three maps' weights stacked as w [3*H*D, hidden]
+ * (row-major, rows W_q, W_k, W_v) and bias [3*H*D] (or NULL):
+ *   q[t,h,d]   = sum_e x[t,e]   w[h*D+d, e]       + bias[h*D+d]
+ *   k[t,h,d]   = sum_e x[t,e]   w[H*D+h*D+d, e]   + bias[H*D+h*D+d]
+ *   v[t,h,d]   = sum_e x[t,e]   w[2*H*D+h*D+d, e] + bias[2*H*D+h*D+d]
+ *   q_r[h,r,d] = sum_e rel[r,e] w[h*D+d, e]       + bias[h*D+d]
+ *   k_r[h,r,d] = sum_e rel[r,e] w[H*D+h*D+d, e]   + bias[H*D+h*D+d]
+ * (the relative-position embedding rows go through the query and key maps:
+ * DeBERTa-v2/v3's shared attention key). x is [tokens, hidden] and rel
+ * [rel_rows, hidden], both row-major with rows of `hidden` elements; q, k, v
+ * are written contiguous [tokens, H, D] (tok_stride H*D, head_stride D, the
+ * layout df_attn_fwd takes) and q_r, k_r contiguous [H, rel_rows, D]. With
+ * rel == NULL (and rel_rows == 0) only q, k, v are written. dtype is DF_BF16
+ * or DF_FP16 for every operand and output (fp32 accumulation; DF_FP32 gives
+ * DF_ERR_UNSUPPORTED); head_dim in {32, 64, 128}; hidden a positive multiple
+ * of 8; x, w and rel 16-byte aligned. All pointers are caller-owned device
+ * pointers; nothing is allocated; work is enqueued on `stream`; errors as
+ * for df_attn_fwd (checked on the host before anything is enqueued). */
+int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim, int32_t rel_rows,
+                int32_t dtype, const void* x, const void* w, const void* bias, const void* rel,
+                void* q, void* k, void* v, void* q_r, void* k_r, void* stream);
+
 /* Static description of an error code. */
 const char* df_strerror(int code);
 

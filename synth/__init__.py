@@ -192,3 +192,37 @@ def workload_inputs(n: int, dtype: Optional[str] = None,
                        w.seed, batch=w.batch, seqlen=w.seqlen,
                        mask_frac=w.mask_frac, std=w.std, with_dout=with_dout,
                        name=w.name)
+
+
+@dataclasses.dataclass
+class ProjInputs:
+    """Inputs of the fused projections, as working-dtype torch tensors (CPU)
+    and float64 copies of the rounded values."""
+
+    tokens: int
+    hidden: int
+    heads: int
+    head_dim: int
+    rows: int
+    dtype: str
+    t: dict
+    f64: dict
+
+
+def make_proj_inputs(tokens: int, hidden: int, heads: int, head_dim: int, rows: int, dtype: str,
+                     seed: int, *, bias: bool = True, rel: bool = True) -> ProjInputs:
+    """Hidden states x ~ N(0, 1) [tokens, hidden], stacked weights
+    w ~ N(0, 1/hidden) [3*heads*head_dim, hidden] (outputs of unit scale),
+    bias ~ N(0, 0.1^2) and relative-position embedding rows rel ~ N(0, 1)
+    [rows, hidden], drawn in float64 in that order and rounded once."""
+    rng = np.random.default_rng(seed)
+    N = 3 * heads * head_dim
+    t, f = {}, {}
+    specs = [("x", (tokens, hidden), 1.0), ("w", (N, hidden), 1.0 / math.sqrt(hidden))]
+    if bias:
+        specs.append(("bias", (N,), 0.1))
+    if rel:
+        specs.append(("rel", (rows, hidden), 1.0))
+    for nm, shape, scale in specs:
+        t[nm], f[nm] = _round(rng.standard_normal(shape) * scale, dtype)
+    return ProjInputs(tokens, hidden, heads, head_dim, rows if rel else 0, dtype, t, f)

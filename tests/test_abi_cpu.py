@@ -172,6 +172,26 @@ def test_bwd_and_index_reject_on_host(df):
     assert L.df_build_rel_index(64, 100, 256, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == 1
 
 
+def test_qkv_proj_rejects_on_host(df):
+    L = df.lib()
+    f = ctypes.c_void_p(FAKE)
+
+    def call(T=64, E=64, H=2, D=32, R=8, dt=0, x=f, w=f, b=f, rel=f, outs=(f,) * 5):
+        return L.df_qkv_proj(T, E, H, D, R, dt, x, w, b, rel, *outs, None)
+    assert call(dt=2) == 2 and "16-bit" in L.df_last_error().decode()
+    assert call(dt=7) == 2
+    assert call(D=48) == 2
+    assert call(H=0) == 1
+    assert call(E=60) == 1 and "multiple of 8" in L.df_last_error().decode()
+    assert call(T=-1) == 1
+    assert call(x=None) == 1 and "x" in L.df_last_error().decode()
+    assert call(w=None) == 1
+    assert call(x=ctypes.c_void_p(FAKE + 8)) == 1          # x must be 16-byte aligned
+    assert call(outs=(f, None, f, f, f)) == 1               # k missing
+    assert call(rel=None) == 1                               # rel_rows > 0 without rel
+    assert call(outs=(f, f, f, None, f)) == 1               # q_r missing while rel given
+
+
 def test_profile_api_without_enable(df):
     L = df.lib()
     ms = (ctypes.c_float * 9)()
