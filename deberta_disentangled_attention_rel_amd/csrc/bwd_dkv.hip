@@ -278,17 +278,33 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         dP = TR::mma(ld_row<TR>(dOs[buf], QP, 32 * u + li, q * KS + g * E), Vf[q], dP);
       }
       float P[16], dS[16];
+      [[maybe_unused]] uint32_t wd[16];
+      if constexpr (DROP) {
+        // This lane's key is word jw % 4 of the call for (query, key group
+        // jw / 4), and the four lanes of a quad hold the four keys of one
+        // group and the same 16 queries. Lane e of the quad computes the
+        // calls of queries 4c + e; a 4 x 4 transpose inside the quad (two
+        // exchange steps) then hands each lane its own word of every call.
+        const int e = lane & 3;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const Philox4 r = philox4x32_10(uint32_t(jw) >> 2, uint32_t(i0 + half_major_partner<NQT>(u, g, 4 * c + e)),
+                                          uint32_t(blk.z * p.H + h), p.drop_off, p.seed_lo, p.seed_hi);
+          uint32_t w0 = r.w[0], w1 = r.w[1], w2 = r.w[2], w3 = r.w[3];
+          quad_transpose(w0, w1, w2, w3, e);
+          wd[4 * c] = w0;
+          wd[4 * c + 1] = w1;
+          wd[4 * c + 2] = w2;
+          wd[4 * c + 3] = w3;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int il = half_major_partner<NQT>(u, g, v);
         P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]) + bj);
         if constexpr (DROP) {
-          // this lane's key is word jw % 4 of the call for (query, key group):
           // dV takes P F, dS = P (F dP - Delta), F = keep / (1 - p)
-          const Philox4 r = philox4x32_10(uint32_t(jw) >> 2, uint32_t(i0 + il), uint32_t(blk.z * p.H + h),
-                                          p.drop_off, p.seed_lo, p.seed_hi);
-          const uint32_t wd = (jw & 2) ? ((jw & 1) ? r.w[3] : r.w[2]) : ((jw & 1) ? r.w[1] : r.w[0]);
-          const float F = wd >= p.drop_thr ? p.drop_scale : 0.f;
+          const float F = wd[v] >= p.drop_thr ? p.drop_scale : 0.f;
           dS[v] = P[v] * (dP[v] * F - dlt_s[buf][il]);
           P[v] *= F;
         } else {

@@ -232,6 +232,43 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return {{c0, c1, c2, c3}};
 }
 
+// 4 x 4 transpose inside each quad of lanes (lanes 4m .. 4m+3): on entry
+// lane e of the quad holds row e of a matrix in (w0, w1, w2, w3), on exit it
+// holds column e. Two exchange steps with the lane 2 apart, then the lane 1
+// apart (quad-permute DPP moves); e = lane % 4.
+__device__ __forceinline__ uint32_t quad_xor(uint32_t x, int ctrl_xor) {
+  // quad_perm [2,3,0,1] (xor 2) = 0x4E, [1,0,3,2] (xor 1) = 0xB1
+  return ctrl_xor == 2 ? uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, false))
+                       : uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3, int e) {
+  // step 1: exchange the off-diagonal 2 x 2 blocks between lanes e and e ^ 2
+  {
+    const bool hi = (e & 2) != 0;
+    const uint32_t x = quad_xor(hi ? w0 : w2, 2), y = quad_xor(hi ? w1 : w3, 2);
+    if (hi) {
+      w0 = x;
+      w1 = y;
+    } else {
+      w2 = x;
+      w3 = y;
+    }
+  }
+  // step 2: exchange the off-diagonal elements of each 2 x 2 block between
+  // lanes e and e ^ 1
+  {
+    const bool odd = (e & 1) != 0;
+    const uint32_t x = quad_xor(odd ? w0 : w1, 1), y = quad_xor(odd ? w2 : w3, 1);
+    if (odd) {
+      w0 = x;
+      w2 = y;
+    } else {
+      w1 = x;
+      w3 = y;
+    }
+  }
+}
+
 // Compile-time flag passed to a generic lambda, so that a loop body can be
 // instantiated once per tile class (band / far) as straight-line code.
 template <bool B> struct BoolC {
