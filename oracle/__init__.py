@@ -11,3 +11,4 @@ from .df_oracle import (  # noqa: F401
 )
 from . import philox  # noqa: F401
 from .proj import qkv_projection  # noqa: F401
+from .pack import pack_padded, unpack_packed  # noqa: F401
