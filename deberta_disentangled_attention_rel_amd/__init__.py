@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "fwd_inference", "bwd",
-           "qkv_proj",
+           "qkv_proj", "pack_padded", "unpack_packed",
            "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
@@ -28,7 +28,8 @@ EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
             "df_attn_fwd", "df_attn_fwd_inference", "df_attn_bwd", "df_attn_fwd_dropout",
             "df_attn_bwd_dropout", "df_strerror", "df_last_error",
             "df_attn_version",
-            "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name", "df_qkv_proj")
+            "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name", "df_qkv_proj",
+            "df_pack_padded", "df_unpack_packed")
 NUM_STAGES = 9
 
 
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.df_attn_bwd.restype = ctypes.c_int
     L.df_qkv_proj.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.df_qkv_proj.restype = ctypes.c_int
+    L.df_pack_padded.argtypes = [i32, i32, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
+    L.df_pack_padded.restype = ctypes.c_int
+    L.df_unpack_packed.argtypes = [i32, i32, ctypes.c_int64, vp, vp, vp, vp, vp]
+    L.df_unpack_packed.restype = ctypes.c_int
     L.df_strerror.argtypes = [ctypes.c_int]
     L.df_strerror.restype = ctypes.c_char_p
     L.df_last_error.argtypes = []
@@ -302,3 +307,39 @@ def qkv_proj(x, w, bias, rel, num_heads: int, head_dim: int, out=None):
     _check(lib().df_qkv_proj(T, E, H, D, R, DTYPE_CODES[x.dtype], _ptr(x), _ptr(w), _ptr(bias), _ptr(rel),
                              _ptr(q), _ptr(k), _ptr(v), _ptr(q_r), _ptr(k_r), _stream(x.device)))
     return q, k, v, q_r, k_r
+
+
+def pack_padded(padded, mask):
+    """Right-padded ``[B, L, ...]`` rows and a ``[B, L]`` mask (nonzero =
+    valid) to packed ``[T, ...]`` rows (``df_pack_padded``). Returns
+    ``(packed, cu_seqlens, max_seqlen)``; reading T and max_seqlen back to the
+    host synchronises the stream."""
+    B, L = mask.shape
+    if padded.shape[:2] != (B, L):
+        raise ValueError("padded must be [B, L, ...] like mask")
+    padded = padded.contiguous()
+    m8 = mask.to(torch.uint8).contiguous()
+    row_bytes = padded[0, 0].numel() * padded.element_size()
+    packed = torch.empty((B * L,) + tuple(padded.shape[2:]), dtype=padded.dtype, device=padded.device)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=padded.device)
+    mx = torch.empty(1, dtype=torch.int32, device=padded.device)
+    _check(lib().df_pack_padded(B, L, row_bytes, _ptr(padded), _ptr(m8), _ptr(packed), _ptr(cu), _ptr(mx),
+                                _stream(padded.device)))
+    T = int(cu[-1].item())
+    return packed[:T], cu, int(mx.item())
+
+
+def unpack_packed(packed, cu_seqlens, mask):
+    """Packed ``[T, ...]`` rows back to ``[B, L, ...]`` (zeros at invalid
+    positions) for the mask they were packed with (``df_unpack_packed``)."""
+    B, L = mask.shape
+    packed = packed.contiguous()
+    m8 = mask.to(torch.uint8).contiguous()
+    row_bytes = packed[0].numel() * packed.element_size() if packed.shape[0] else \
+        int(torch.tensor(packed.shape[1:]).prod().item()) * packed.element_size()
+    out = torch.empty((B, L) + tuple(packed.shape[1:]), dtype=packed.dtype, device=packed.device)
+    src = packed if packed.shape[0] else torch.empty((1,) + tuple(packed.shape[1:]), dtype=packed.dtype,
+                                                     device=packed.device)
+    _check(lib().df_unpack_packed(B, L, row_bytes, _ptr(src), _ptr(m8), _ptr(cu_seqlens.contiguous()), _ptr(out),
+                                  _stream(packed.device)))
+    return out

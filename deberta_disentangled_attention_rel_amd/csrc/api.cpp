@@ -590,3 +590,51 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Packing helpers for the packed layout.
+
+namespace {
+
+int check_pack_args(int32_t batch, int32_t max_len, int64_t row_bytes, const void* a, const char* an,
+                    const uint8_t* mask, const void* b, const char* bn, const int32_t* cu) {
+  if (batch < 1) return fail(DF_ERR_INVALID, "batch must be >= 1, got %d", batch);
+  if (max_len < 1) return fail(DF_ERR_INVALID, "max_len must be >= 1, got %d", max_len);
+  if (int64_t(batch) * max_len >= (int64_t(1) << 31))
+    return fail(DF_ERR_INVALID, "batch * max_len must be < 2^31");
+  if (row_bytes < 16 || row_bytes % 16)
+    return fail(DF_ERR_INVALID, "row_bytes must be a positive multiple of 16, got %lld", (long long)row_bytes);
+  int rc;
+  if ((rc = check_ptr(a, an, 16)) || (rc = check_ptr(b, bn, 16)) || (rc = check_ptr(mask, "mask", 1)) ||
+      (rc = check_ptr(cu, "cu_seqlens", 4)))
+    return rc;
+  return DF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int df_pack_padded(int32_t batch, int32_t max_len, int64_t row_bytes, const void* padded, const uint8_t* mask,
+                   void* packed, int32_t* cu_seqlens, int32_t* max_seqlen, void* stream) {
+  int rc = check_pack_args(batch, max_len, row_bytes, padded, "padded", mask, packed, "packed", cu_seqlens);
+  if (rc) return rc;
+  if ((rc = hip_check(dfa::launch_pack(batch, max_len, row_bytes, padded, mask, packed, cu_seqlens, max_seqlen,
+                                       (hipStream_t)stream),
+                      "pack")))
+    return rc;
+  return ok();
+}
+
+int df_unpack_packed(int32_t batch, int32_t max_len, int64_t row_bytes, const void* packed, const uint8_t* mask,
+                     const int32_t* cu_seqlens, void* padded, void* stream) {
+  int rc = check_pack_args(batch, max_len, row_bytes, packed, "packed", mask, padded, "padded", cu_seqlens);
+  if (rc) return rc;
+  if ((rc = hip_check(dfa::launch_unpack(batch, max_len, row_bytes, packed, mask, cu_seqlens, padded,
+                                         (hipStream_t)stream),
+                      "unpack")))
+    return rc;
+  return ok();
+}
+
+}  // extern "C"

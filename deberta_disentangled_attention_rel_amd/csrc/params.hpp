@@ -85,5 +85,9 @@ hipError_t launch_relgrad_dx(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_dw(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_sum(const Params& p, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);
+hipError_t launch_pack(int B, int L, int64_t row_bytes, const void* padded, const uint8_t* mask, void* packed,
+                       int32_t* cu, int32_t* max_len, hipStream_t st);
+hipError_t launch_unpack(int B, int L, int64_t row_bytes, const void* packed, const uint8_t* mask,
+                         const int32_t* cu, void* padded, hipStream_t st);
 
 }  // namespace dfa

@@ -195,6 +195,31 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
                 int32_t dtype, const void* x, const void* w, const void* bias, const void* rel,
                 void* q, void* k, void* v, void* q_r, void* k_r, void* stream);
 
+
+/* Packing helpers for the packed layout (DisentangledFlash 1.1.1 page,
+ * "Packed unpadded inference and training": right-padded [B, L, ...] input
+ * becomes FlashAttention-style [total_tokens, ...] rows with cu_seqlens, and
+ * the packed output goes back). Rows are opaque: row_bytes bytes each (a
+ * positive multiple of 16), padded is [batch, max_len] rows, mask uint8
+ * [batch, max_len] (nonzero = valid token). Sequence b's length is the
+ * number of valid tokens in mask row b, and its valid tokens, in order,
+ * become packed rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (for a right-padded
+ * mask: its first tokens, the layout df_attn_fwd takes with cu_seqlens).
+ *
+ * df_pack_padded writes packed (capacity batch*max_len rows; only the first
+ * cu_seqlens[batch] are written), cu_seqlens int32 [batch+1] and, unless
+ * NULL, the largest length into *max_seqlen (an int32 in device memory).
+ * df_unpack_packed writes every row of padded: the packed row of each valid
+ * position, zeros elsewhere (cu_seqlens as written by df_pack_padded for
+ * the same mask). All pointers are caller-owned device pointers (padded and
+ * packed 16-byte aligned); work is enqueued on `stream`; host-side checks
+ * and error codes as for df_attn_fwd. */
+int df_pack_padded(int32_t batch, int32_t max_len, int64_t row_bytes, const void* padded,
+                   const uint8_t* mask, void* packed, int32_t* cu_seqlens, int32_t* max_seqlen,
+                   void* stream);
+int df_unpack_packed(int32_t batch, int32_t max_len, int64_t row_bytes, const void* packed,
+                     const uint8_t* mask, const int32_t* cu_seqlens, void* padded, void* stream);
+
 /* Static description of an error code. */
 const char* df_strerror(int code);
 

@@ -192,6 +192,19 @@ def test_qkv_proj_rejects_on_host(df):
     assert call(outs=(f, f, f, None, f)) == 1               # q_r missing while rel given
 
 
+def test_pack_helpers_reject_on_host(df):
+    L = df.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert L.df_pack_padded(0, 8, 16, f, f, f, f, None, None) == 1
+    assert L.df_pack_padded(2, 0, 16, f, f, f, f, None, None) == 1
+    assert L.df_pack_padded(2, 8, 24, f, f, f, f, None, None) == 1 and "multiple of 16" in L.df_last_error().decode()
+    assert L.df_pack_padded(2, 8, 16, None, f, f, f, None, None) == 1
+    assert L.df_pack_padded(2, 8, 16, f, f, ctypes.c_void_p(FAKE + 8), f, None, None) == 1
+    assert L.df_pack_padded(2, 8, 16, f, f, f, None, None, None) == 1
+    assert L.df_unpack_packed(2, 8, 16, f, None, f, f, None) == 1
+    assert L.df_unpack_packed(1 << 16, 1 << 15, 16, f, f, f, f, None) == 1   # batch * max_len >= 2^31
+
+
 def test_profile_api_without_enable(df):
     L = df.lib()
     ms = (ctypes.c_float * 9)()
