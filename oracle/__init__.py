@@ -6,7 +6,7 @@ The product path (the HIP library and its Python binding) never imports it and
 shares no code with it.
 """
 from .df_oracle import (  # noqa: F401
-    att_and_rows, bucket_exact, delta, rel_luts, sequences, scores,
+    att_and_rows, bucket_exact, delta, p2c_rows, P2C_CONVENTIONS, rel_luts, sequences, scores,
     forward, backward, forward_rows, dq_rows,
 )
 from . import philox  # noqa: F401

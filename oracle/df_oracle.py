@@ -107,6 +107,23 @@ def delta(rel: np.ndarray, span: int, buckets: int) -> np.ndarray:
     return _delta_table(lo, hi, span, buckets)[rel - lo]
 
 
+P2C_CONVENTIONS = ("literal", "shared")
+
+
+def p2c_rows(rel: np.ndarray, span: int, buckets: int, p2c: str = "literal") -> np.ndarray:
+    """Row of Q_r that pair (i, j) uses, for ``rel = i - j``.
+
+    ``"literal"``: ``delta(j, i)``, the P2C index as the method's score formula
+    writes it. ``"shared"``: ``delta(i, j)``, the same row as C2P, which is
+    how deployed DeBERTa-v2/v3 code indexes P2C in self-attention (only this
+    index changes between the two)."""
+    if p2c == "literal":
+        return delta(-np.asarray(rel), span, buckets)
+    if p2c == "shared":
+        return delta(np.asarray(rel), span, buckets)
+    raise ValueError(f"unknown P2C convention {p2c!r}")
+
+
 def rel_luts(max_seqlen: int, span: int, buckets: int) -> tuple:
     """The two relative-index tables over ``d = i - j``.
 
@@ -142,7 +159,7 @@ def _valid(key_mask, st: int, en: int) -> np.ndarray:
     return np.asarray(key_mask[st:en]).astype(bool)
 
 
-def scores(Q, K, q_r_h, k_r_h, span: int, buckets: int) -> np.ndarray:
+def scores(Q, K, q_r_h, k_r_h, span: int, buckets: int, p2c: str = "literal") -> np.ndarray:
     """Unmasked score matrix ``S[i, j]`` for one sequence and one head.
 
     ``Q, K`` are ``[L, D]``; ``q_r_h, k_r_h`` are ``[R, D]``. The two L x R
@@ -153,12 +170,12 @@ def scores(Q, K, q_r_h, k_r_h, span: int, buckets: int) -> np.ndarray:
     idx = np.arange(L)
     rel = idx[:, None] - idx[None, :]
     ci = delta(rel, span, buckets)          # delta(i, j)
-    pi = delta(-rel, span, buckets)         # delta(j, i)
+    pi = p2c_rows(rel, span, buckets, p2c)  # delta(j, i) (literal) or delta(i, j) (shared)
     c2p_full = Q @ k_r_h.T                  # [L, R]: Q_i . K_r[r]
     p2c_full = K @ q_r_h.T                  # [L, R]: K_j . Q_r[r]
     c2p = np.take_along_axis(c2p_full, ci, axis=1)          # [i, j] -> row i
-    p2c = p2c_full[idx[None, :], pi]                         # [i, j] -> row j
-    return s * (Q @ K.T + c2p + p2c)
+    p2c_term = p2c_full[idx[None, :], pi]                    # [i, j] -> row j
+    return s * (Q @ K.T + c2p + p2c_term)
 
 
 def _probs(S: np.ndarray, valid: np.ndarray) -> tuple:
@@ -192,7 +209,7 @@ def _dropout_factor(dropout, n, h, H, L):
 
 def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
             cu_seqlens=None, batch=None, seqlen=None, return_probs: bool = False,
-            heads=None, dropout=None):
+            heads=None, dropout=None, p2c: str = "literal"):
     """Output ``[T, H, D]`` and LSE ``[H, T]`` (natural log), float64.
 
     ``q, k, v`` are ``[T, H, D]``; ``q_r, k_r`` are ``[H, R, D]``.
@@ -200,7 +217,7 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
     0 / -inf). With ``return_probs`` also returns ``{(seq, head): P}``.
     ``dropout = (p, seed, offset)`` applies attention-probability dropout
     after the softmax: out = (P * keep / (1 - p)) V; the LSE is that of the
-    undropped scores.
+    undropped scores. ``p2c`` selects the P2C row convention (:func:`p2c_rows`).
     """
     q, k, v, q_r, k_r = (np.asarray(x, dtype=np.float64) for x in (q, k, v, q_r, k_r))
     T, H, D = q.shape
@@ -213,7 +230,7 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
     for n, (st, en) in enumerate(sequences(T, cu_seqlens, batch, seqlen)):
         valid = _valid(key_mask, st, en)
         for h in hs:
-            S = scores(q[st:en, h], k[st:en, h], q_r[h], k_r[h], span, buckets)
+            S = scores(q[st:en, h], k[st:en, h], q_r[h], k_r[h], span, buckets, p2c)
             P, l = _probs(S, valid)
             out[st:en, h] = (P * _dropout_factor(dropout, n, h, H, en - st)) @ v[st:en, h]
             lse[h, st:en] = l
@@ -229,7 +246,7 @@ def forward(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None,
 
 def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
              cu_seqlens=None, batch=None, seqlen=None, heads=None,
-             return_strips: bool = False, dropout=None):
+             return_strips: bool = False, dropout=None, p2c: str = "literal"):
     """Gradients of ``sum(out * dout)``: ``dq, dk, dv, dq_r, dk_r``, float64.
 
     Follows the chain rule of the forward step by step: dV = P^T dO,
@@ -263,10 +280,10 @@ def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
         idx = np.arange(L)
         rel = idx[:, None] - idx[None, :]
         ci = delta(rel, span, buckets)
-        pi = delta(-rel, span, buckets)
+        pi = p2c_rows(rel, span, buckets, p2c)
         for h in hs:
             Q, K, V, dO = q[st:en, h], k[st:en, h], v[st:en, h], dout[st:en, h]
-            S = scores(Q, K, q_r[h], k_r[h], span, buckets)
+            S = scores(Q, K, q_r[h], k_r[h], span, buckets, p2c)
             P, _ = _probs(S, valid)
             F = _dropout_factor(dropout, n, h, H, L)
             dV = (P * F).T @ dO
@@ -295,7 +312,7 @@ def backward(q, k, v, q_r, k_r, dout, span: int, buckets: int, key_mask=None,
 # ----------------------------------------------------------------------------
 # row-sampled evaluation (large workloads)
 
-def _row_scores(Q, K, q_r_h, k_r_h, rows, span, buckets):
+def _row_scores(Q, K, q_r_h, k_r_h, rows, span, buckets, p2c="literal"):
     """``S[rows, :]`` for one sequence and head, without the full L x L matrix."""
     L, D = K.shape
     s = 1.0 / math.sqrt(3.0 * D)
@@ -303,21 +320,21 @@ def _row_scores(Q, K, q_r_h, k_r_h, rows, span, buckets):
     jdx = np.arange(L)
     rel = rows[:, None] - jdx[None, :]
     ci = delta(rel, span, buckets)
-    pi = delta(-rel, span, buckets)
+    pi = p2c_rows(rel, span, buckets, p2c)
     c2p_full = Q[rows] @ k_r_h.T
     p2c_full = K @ q_r_h.T
     c2p = np.take_along_axis(c2p_full, ci, axis=1)
-    p2c = p2c_full[jdx[None, :], pi]
-    return s * (Q[rows] @ K.T + c2p + p2c), ci
+    p2c_term = p2c_full[jdx[None, :], pi]
+    return s * (Q[rows] @ K.T + c2p + p2c_term), ci
 
 
 def forward_rows(q, k, v, q_r, k_r, span, buckets, seq: tuple, head: int,
-                 rows, key_mask=None):
+                 rows, key_mask=None, p2c="literal"):
     """Output and LSE of the given local query ``rows`` of one sequence/head."""
     st, en = seq
     Q, K, V = (np.asarray(x[st:en, head], dtype=np.float64) for x in (q, k, v))
     S, _ = _row_scores(Q, K, np.asarray(q_r[head], np.float64),
-                       np.asarray(k_r[head], np.float64), rows, span, buckets)
+                       np.asarray(k_r[head], np.float64), rows, span, buckets, p2c)
     valid = _valid(key_mask, st, en)
     rows = np.asarray(rows)
     Sm = np.where(valid[rows][:, None] & valid[None, :], S, -np.inf)
@@ -333,7 +350,7 @@ def forward_rows(q, k, v, q_r, k_r, span, buckets, seq: tuple, head: int,
 
 
 def dq_rows(q, k, v, q_r, k_r, dout, span, buckets, seq: tuple, head: int,
-            rows, key_mask=None):
+            rows, key_mask=None, p2c="literal"):
     """dQ of the given local query ``rows`` of one sequence/head.
 
     A row of dQ needs only its own rows of S, P, dP and dS, and its own row
@@ -347,7 +364,7 @@ def dq_rows(q, k, v, q_r, k_r, dout, span, buckets, seq: tuple, head: int,
     R = k_r_h.shape[0]
     s = 1.0 / math.sqrt(3.0 * D)
     S, ci = _row_scores(Q, K, np.asarray(q_r[head], np.float64), k_r_h, rows,
-                        span, buckets)
+                        span, buckets, p2c)
     valid = _valid(key_mask, st, en)
     rows = np.asarray(rows)
     out = np.zeros((len(rows), D))

@@ -412,3 +412,83 @@ def test_workload_recipes():
     lens = synth.packed_lengths(rng, 16384, 64, 2048)
     assert sum(lens) == 16384 and all(n <= 2048 for n in lens[:-1]) and all(n >= 64 for n in lens[:-1])
     assert WORKLOADS[3].batch * WORKLOADS[3].seqlen == 16384
+
+
+# ----------------------------------------------------------------------------
+# P11: the shared P2C convention (the row C2P uses, as deployed DeBERTa code
+# indexes P2C in self-attention), pinned like the literal one: per-element
+# loops, finite differences, and the reflection that links the two index
+# functions where no clamp is reached.
+
+def _brute_shared_scores(Q, K, Qr, Kr, span, buckets):
+    L, D = len(Q), len(Q[0])
+    att, R = oracle.att_and_rows(span, buckets)
+    s = 1.0 / math.sqrt(3 * D)
+
+    def dl(a, b):
+        return min(max(bucket_decimal(a - b, span, buckets) + att, 0), R - 1)
+
+    S = np.zeros((L, L))
+    for i in range(L):
+        for j in range(L):
+            c = dl(i, j)   # both terms use delta(i, j)
+            S[i, j] = s * sum(Q[i][d] * K[j][d] + Q[i][d] * Kr[c][d] + K[j][d] * Qr[c][d] for d in range(D))
+    return S
+
+
+@pytest.mark.parametrize("span,buckets,L", [(6, 0, 14), (12, 8, 16), (81, 10, 16)])
+def test_p11_shared_brute_force(span, buckets, L):
+    inp = _small(L=L, H=1, D=4, span=span, buckets=buckets, seed=21)
+    f = inp.f64
+    args = [f["q"][:, 0].tolist(), f["k"][:, 0].tolist(), f["q_r"][0].tolist(), f["k_r"][0].tolist()]
+    S = _brute_shared_scores(*args, span, buckets)
+    S2 = oracle.scores(f["q"][:, 0], f["k"][:, 0], f["q_r"][0], f["k_r"][0], span, buckets, "shared")
+    assert np.abs(S - S2).max() < 1e-12
+    S3 = oracle.scores(f["q"][:, 0], f["k"][:, 0], f["q_r"][0], f["k_r"][0], span, buckets, "literal")
+    assert np.abs(S - S3).max() > 1e-3   # the conventions differ
+
+
+def test_p11_shared_reflection():
+    """Unbucketed, L <= span: no clamp is reached, the literal row is
+    att - d and the shared row att + d = R - (att - d); so the shared scores
+    with Q_r equal the literal scores with Q_r'[r] = Q_r[R - r]."""
+    span, L, D = 20, 16, 4
+    att, R = oracle.att_and_rows(span, 0)
+    rng = np.random.default_rng(4)
+    Q, K = rng.standard_normal((L, D)), rng.standard_normal((L, D))
+    Qr, Kr = rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    Qr2 = np.zeros_like(Qr)
+    Qr2[1:] = Qr[R - np.arange(1, R)]
+    S_sh = oracle.scores(Q, K, Qr, Kr, span, 0, "shared")
+    S_li = oracle.scores(Q, K, Qr2, Kr, span, 0, "literal")
+    assert np.abs(S_sh - S_li).max() < 1e-13
+
+
+def test_p11_shared_finite_differences():
+    inp = _small(H=2, D=4, span=12, buckets=8, seed=6, mask_frac=0.2, lengths=[13, 19])
+    f = {k: v.copy() for k, v in inp.f64.items()}
+    w = inp.workload
+    W = f["dout"]
+    kw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq, p2c="shared")
+
+    def loss(ff):
+        o, _ = oracle.forward(ff["q"], ff["k"], ff["v"], ff["q_r"], ff["k_r"], w.span, w.buckets, **kw)
+        return float((o * W).sum())
+
+    grads = oracle.backward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], W, w.span, w.buckets, **kw)
+    rng = np.random.default_rng(1)
+    eps = 1e-6
+    for name, g in zip(("q", "k", "v", "q_r", "k_r"), grads):
+        x = f[name]
+        flat = rng.choice(x.size, size=min(40, x.size), replace=False)
+        num = np.zeros(len(flat))
+        for n, e in enumerate(flat):
+            idx = np.unravel_index(e, x.shape)
+            old = x[idx]
+            x[idx] = old + eps
+            lp = loss(f)
+            x[idx] = old - eps
+            lm = loss(f)
+            x[idx] = old
+            num[n] = (lp - lm) / (2 * eps)
+        assert np.linalg.norm(g.ravel()[flat] - num) <= 1e-6 * max(np.linalg.norm(num), 1e-30), name
