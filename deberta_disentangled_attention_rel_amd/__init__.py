@@ -45,7 +45,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+                ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("p2c_convention", ctypes.c_int32)]
 
 
 _lib = None
@@ -127,12 +128,17 @@ def _as_thd(x: torch.Tensor) -> torch.Tensor:
     return x
 
 
-def make_shape(q: torch.Tensor, batch: int, max_seqlen: int) -> Shape:
+P2C_CONVENTIONS = {"literal": 0, "shared": 1}
+
+
+def make_shape(q: torch.Tensor, batch: int, max_seqlen: int, p2c: str = "literal") -> Shape:
     T, H, D = q.shape
     if q.dtype not in DTYPE_CODES:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    if p2c not in P2C_CONVENTIONS:
+        raise ValueError(f"p2c must be one of {sorted(P2C_CONVENTIONS)}")
     return Shape(int(batch), int(max_seqlen), int(T), int(H), int(D), DTYPE_CODES[q.dtype],
-                 int(q.stride(0)), int(q.stride(1)))
+                 int(q.stride(0)), int(q.stride(1)), P2C_CONVENTIONS[p2c])
 
 
 def _layout(q, k, v, cu_seqlens, max_seqlen):
@@ -197,12 +203,13 @@ def _workspace(pass_, shape, span, buckets, device, workspace):
 
 def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=None,
         max_seqlen: Optional[int] = None, out=None, lse=None, workspace=None,
-        dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+        dropout_p: float = 0.0, seed: int = 0, offset: int = 0, p2c: str = "literal"):
     """Forward pass. Returns ``(out, lse)`` with ``out`` shaped like ``q``.
     ``dropout_p > 0`` applies attention-probability dropout (mask from
-    ``(seed, offset)``; pass the same values to ``bwd``)."""
+    ``(seed, offset)``; pass the same values to ``bwd``). ``p2c`` is the P2C
+    row convention: "literal" (delta(j, i)) or "shared" (the C2P row)."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
-    shape = make_shape(q3, batch, L)
+    shape = make_shape(q3, batch, L, p2c)
     T, H, D = q3.shape
     if out is None:
         out = torch.empty_like(q3)
@@ -226,10 +233,10 @@ def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=No
 
 
 def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=None,
-                  max_seqlen: Optional[int] = None, out=None, workspace=None):
+                  max_seqlen: Optional[int] = None, out=None, workspace=None, p2c: str = "literal"):
     """Inference forward (no LSE, nothing kept for a backward). Returns ``out``."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
-    shape = make_shape(q3, batch, L)
+    shape = make_shape(q3, batch, L, p2c)
     if out is None:
         out = torch.empty_like(q3)
     out3 = _as_thd(out)
@@ -246,11 +253,11 @@ def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_
 
 def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=None,
         cu_seqlens=None, max_seqlen: Optional[int] = None, grads=None, workspace=None,
-        dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+        dropout_p: float = 0.0, seed: int = 0, offset: int = 0, p2c: str = "literal"):
     """Backward pass. Returns ``(dq, dk, dv, dq_r, dk_r)``. The dropout
-    arguments must be those of the forward that produced ``out``."""
+    arguments and ``p2c`` must be those of the forward that produced ``out``."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
-    shape = make_shape(q3, batch, L)
+    shape = make_shape(q3, batch, L, p2c)
     out3, dout3 = _as_thd(out).contiguous(), _as_thd(dout).contiguous()
     if grads is None:
         grads = (torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3),

@@ -56,6 +56,9 @@ int check_shape(const df_attn_shape* s) {
   if (!s) return fail(DF_ERR_INVALID, "shape is NULL");
   if (s->dtype != DF_BF16 && s->dtype != DF_FP16 && s->dtype != DF_FP32)
     return fail(DF_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+  if (s->p2c_convention != DF_P2C_LITERAL && s->p2c_convention != DF_P2C_SHARED)
+    return fail(DF_ERR_INVALID, "p2c_convention must be DF_P2C_LITERAL (0) or DF_P2C_SHARED (1), got %d",
+                s->p2c_convention);
   if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
     return fail(DF_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128, got %d", s->head_dim);
   if (s->batch < 1) return fail(DF_ERR_INVALID, "batch must be >= 1, got %d", s->batch);
@@ -105,7 +108,7 @@ int check_all(const df_attn_shape* s, int32_t span, int32_t buckets, bool packed
 
 // Workspace plan. Offsets are relative to the workspace base.
 struct Plan {
-  size_t lut, lutp, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
+  size_t lut, lutp, qr_rev, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
   int RP, nchunk, chunk_tokens;
 };
 
@@ -122,6 +125,7 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
   };
   pl.lut = take(2 * (2 * size_t(s->max_seqlen) - 1) * sizeof(int32_t));
   pl.lutp = take((2 * size_t(s->max_seqlen) - 1 + 2 * dfa::kLutPad) * sizeof(uint32_t));
+  pl.qr_rev = s->p2c_convention == DF_P2C_SHARED ? take(H * size_t(R) * D * es) : 0;
   pl.c2ps = take(H * T * pl.RP * es);
   pl.p2cs = take(H * T * pl.RP * es);
   pl.ends = take(4 * H * T * es);
@@ -209,6 +213,7 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
   // narrow kernels keep both rows of a table entry as 16-bit byte offsets
   const size_t esize = s->dtype == DF_FP32 ? 4 : 2;
   p.narrow = (narrow_tables(span, buckets) && size_t(R - 1) * esize <= 0xffff) ? 1 : 0;
+  p.p2c_shared = s->p2c_convention == DF_P2C_SHARED ? 1 : 0;
   p.d_hi = far_bound(span, buckets, s->max_seqlen);
   p.d_lo = -p.d_hi;
   p.c2ps = ws + pl.c2ps;
@@ -222,6 +227,16 @@ dfa::Params base_params(const df_attn_shape* s, int32_t span, int32_t buckets, i
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return DF_OK;
+}
+
+// Index tables, and for the shared P2C convention the reversed q_r the
+// kernels then read (p.qr is redirected to it).
+hipError_t launch_index(dfa::Params& p, int span, int buckets, char* ws, const Plan& pl, hipStream_t st) {
+  hipError_t e = dfa::launch_lut(p.Lmax, span, buckets, p.p2c_shared, p.c2p, p.p2c, const_cast<uint32_t*>(p.lutp), st);
+  if (e != hipSuccess || !p.p2c_shared) return e;
+  e = dfa::launch_reverse_rows(p.qr, ws + pl.qr_rev, p.H, p.R, p.D, p.dtype == dfa::DF_FP32_T ? 4 : 2, st);
+  p.qr = ws + pl.qr_rev;
+  return e;
 }
 
 // Optional per-launch event timing (df_attn_profile_*).
@@ -333,7 +348,7 @@ int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets, int32_
   int rc = index_params(span, buckets, &att, &R);
   if (rc) return rc;
   if (!c2p_lut || !p2c_lut) return fail(DF_ERR_INVALID, "table pointers must not be NULL");
-  rc = hip_check(dfa::launch_lut(max_seqlen, span, buckets, c2p_lut, p2c_lut, nullptr, (hipStream_t)stream),
+  rc = hip_check(dfa::launch_lut(max_seqlen, span, buckets, 0, c2p_lut, p2c_lut, nullptr, (hipStream_t)stream),
                  "relative index kernel");
   return rc ? rc : ok();
 }
@@ -390,7 +405,7 @@ int fwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T == 0) return ok();
   if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                     [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, const_cast<uint32_t*>(p.lutp), st); })) ||
+                     [&] { return launch_index(p, span, buckets, (char*)workspace, pl, st); })) ||
       (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
       (rc = run_stage(DF_STAGE_FWD, st, "forward kernel", [&] { return dfa::launch_fwd(p, st); })))
     return rc;
@@ -466,7 +481,7 @@ int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T > 0) {
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                       [&] { return dfa::launch_lut(p.Lmax, span, buckets, p.c2p, p.p2c, const_cast<uint32_t*>(p.lutp), st); })) ||
+                       [&] { return launch_index(p, span, buckets, (char*)workspace, pl, st); })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
         (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||

@@ -76,7 +76,7 @@ __device__ int bucket_of(int d, int span, int buckets) {
   return d < 0 ? -b : b;
 }
 
-__global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict__ c2p,
+__global__ void lut_kernel(int Lmax, int span, int buckets, int p2c_shared, int32_t* __restrict__ c2p,
                            int32_t* __restrict__ p2c, uint32_t* __restrict__ packed) {
   // with `packed`, thread n also writes entry n of the padded packed table
   // (kLutPad entries on each side repeat the end entries)
@@ -90,7 +90,9 @@ __global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict_
   // bucket is odd, so the P2C row needs no second evaluation
   const int b = bucket_of(d, span, buckets);
   int c = b + att;
-  int p = att - b;
+  // literal P2C row delta(j, i) = att - bucket(d); the shared convention's
+  // row delta(i, j) in reversed coordinates R - 1 - (att + bucket(d))
+  int p = p2c_shared ? att - 1 - b : att - b;
   c = c < 0 ? 0 : (c > R - 1 ? R - 1 : c);
   p = p < 0 ? 0 : (p > R - 1 ? R - 1 : p);
   const int m = n - pad;
@@ -103,10 +105,32 @@ __global__ void lut_kernel(int Lmax, int span, int buckets, int32_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, uint32_t* packed,
+hipError_t launch_lut(int Lmax, int span, int buckets, int p2c_shared, int32_t* c2p, int32_t* p2c, uint32_t* packed,
                       hipStream_t st) {
   const int n = 2 * Lmax - 1 + (packed ? 2 * kLutPad : 0);
-  lut_kernel<<<(n + 255) / 256, 256, 0, st>>>(Lmax, span, buckets, c2p, p2c, packed);
+  lut_kernel<<<(n + 255) / 256, 256, 0, st>>>(Lmax, span, buckets, p2c_shared, c2p, p2c, packed);
+  return hipGetLastError();
+}
+
+// dst[h][r][:] = src[h][R - 1 - r][:] for contiguous [H][R][D] rows (the
+// shared P2C convention's reversed q_r), 16 bytes per thread.
+namespace {
+__global__ void reverse_rows_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int H, int R,
+                                    int chunks_per_row) {
+  const int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(H) * R * chunks_per_row;
+  if (n >= total) return;
+  const int64_t row = n / chunks_per_row, c = n % chunks_per_row;
+  const int64_t h = row / R, r = row % R;
+  dst[n] = src[(h * R + (R - 1 - r)) * chunks_per_row + c];
+}
+}  // namespace
+
+hipError_t launch_reverse_rows(const void* src, void* dst, int H, int R, int D, int elem_bytes, hipStream_t st) {
+  const int cpr = D * elem_bytes / 16;
+  const int64_t total = int64_t(H) * R * cpr;
+  if (total == 0) return hipSuccess;
+  reverse_rows_kernel<<<unsigned((total + 255) / 256), 256, 0, st>>>((const uint4*)src, (uint4*)dst, H, R, cpr);
   return hipGetLastError();
 }
 

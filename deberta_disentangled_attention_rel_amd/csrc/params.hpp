@@ -32,6 +32,11 @@ struct Params {
   const uint32_t* lutp;
   int d_hi, d_lo;           // far field: both tables at their end rows iff d >= d_hi or d <= d_lo
   int narrow;               // 1 if neither table ever steps by more than one row
+  // 1: the shared P2C convention (P2C uses the row C2P uses). The kernels
+  // then see q_r with its rows reversed (qr points at that copy) and a P2C
+  // table in reversed coordinates, clamp(att - 1 - bucket(d)), which is
+  // non-increasing in d like the literal one; dq_r is written back reversed.
+  int p2c_shared;
   // user tensors
   const void *q, *k, *v, *qr, *kr;
   void* out;
@@ -74,8 +79,9 @@ struct ProjParams {
 };
 
 // launchers (each returns hipGetLastError() after its launches)
-hipError_t launch_lut(int Lmax, int span, int buckets, int32_t* c2p, int32_t* p2c, uint32_t* packed,
+hipError_t launch_lut(int Lmax, int span, int buckets, int p2c_shared, int32_t* c2p, int32_t* p2c, uint32_t* packed,
                       hipStream_t st);  // packed may be null
+hipError_t launch_reverse_rows(const void* src, void* dst, int H, int R, int D, int elem_bytes, hipStream_t st);
 hipError_t launch_strips(const Params& p, hipStream_t st);  // both strips
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);

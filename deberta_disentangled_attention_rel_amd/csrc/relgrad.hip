@@ -225,7 +225,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
   float s = 0.f;
   for (int c = 0; c < p.nchunk; ++c) s += part[c * per];
   T* out = (T*)(which ? p.dqr : p.dkr);
-  out[h * per + e] = TR::from_f(s * p.scale);
+  // dq_r of the shared P2C convention was accumulated in reversed row order
+  const int64_t e_out = (which && p.p2c_shared) ? (int64_t(p.R - 1) - e / p.D) * p.D + e % p.D : e;
+  out[h * per + e_out] = TR::from_f(s * p.scale);
 }
 
 template <int DT, int D>

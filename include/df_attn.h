@@ -10,6 +10,7 @@
  * i (query) and j (key):
  *
  *   S[i,j] = s * ( Q_i.K_j + Q_i.K_r[delta(i,j)] + K_j.Q_r[delta(j,i)] ),
+ *   (with p2c_convention = DF_P2C_SHARED the last index is delta(i,j)),
  *   s = 1/sqrt(3*head_dim),
  *   delta(a,b) = clamp(bucket(a-b) + att, 0, R-1),  R = 2*att,
  *   att = buckets > 0 ? buckets : span,
@@ -67,6 +68,13 @@ enum {
   DF_ERR_HIP = 4           /* a HIP launch reported an error */
 };
 
+/* Which row of Q_r the P2C term of pair (query i, key j) uses:
+ * DF_P2C_LITERAL: delta(j, i), the score formula as written above;
+ * DF_P2C_SHARED:  delta(i, j), the row C2P uses, which is how deployed
+ *                 DeBERTa-v2/v3 code indexes P2C in self-attention (for
+ *                 parity with its checkpoints). Only this index changes. */
+enum { DF_P2C_LITERAL = 0, DF_P2C_SHARED = 1 };
+
 typedef struct {
   int32_t batch;          /* number of sequences (padded: B) */
   int32_t max_seqlen;     /* L (padded) or the longest sequence (packed) */
@@ -76,6 +84,7 @@ typedef struct {
   int32_t dtype;          /* df_dtype of q,k,v,q_r,k_r,out,dout and all gradients */
   int64_t tok_stride;     /* element stride between tokens of [T,H,D] tensors */
   int64_t head_stride;    /* element stride between heads of [T,H,D] tensors */
+  int32_t p2c_convention; /* DF_P2C_LITERAL (0) or DF_P2C_SHARED (1) */
 } df_attn_shape;
 
 /* Non-raising eligibility check (the strict-contract idea of the
@@ -96,6 +105,8 @@ size_t df_attn_workspace_size(int pass, const df_attn_shape* shape,
  *   c2p_lut[.] = delta(i, j)  (row of K_r used by query i against key j)
  *   p2c_lut[.] = delta(j, i)  (row of Q_r used by key j against query i)
  * Both are int32 device arrays of 2*max_seqlen-1 entries, written on `stream`.
+ * (These are the DF_P2C_LITERAL tables; under DF_P2C_SHARED the P2C row of a
+ * pair is its c2p_lut entry.)
  * The ceiling of the log bucket is evaluated in fp64 with exact detection of
  * integer arguments, so the tables are exact for every configuration whose
  * ceiling arguments are not within ~1e-12 of an integer without being one. */

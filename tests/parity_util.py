@@ -25,11 +25,11 @@ def to_dev(inp, dev="cuda"):
     return t, km, cu
 
 
-def run_gpu(inp, backward=True, dev="cuda"):
+def run_gpu(inp, backward=True, dev="cuda", p2c="literal"):
     import deberta_disentangled_attention_rel_amd as df
     w = inp.workload
     t, km, cu = to_dev(inp, dev)
-    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen, p2c=p2c)
     out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
     res = {"out": out, "lse": lse}
     if backward:
@@ -40,10 +40,10 @@ def run_gpu(inp, backward=True, dev="cuda"):
     return {k: v.float().cpu().numpy() for k, v in res.items()}
 
 
-def run_oracle(inp, backward=True):
+def run_oracle(inp, backward=True, p2c="literal"):
     f = inp.f64
     w = inp.workload
-    kw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq)
+    kw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq, p2c=p2c)
     out, lse = oracle.forward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], w.span, w.buckets, **kw)
     res = {"out": out, "lse": lse}
     if backward:

@@ -71,6 +71,8 @@ def _shape(df, **kw):
     (dict(), 512, 1, 1),                           # buckets must be 0 or >= 2
     (dict(), 100, 256, 1),                         # span - 1 <= buckets / 2
     (dict(), 512, -2, 1),
+    (dict(p2c_convention=1), 512, 256, 0),
+    (dict(p2c_convention=2), 512, 256, 1),         # unknown P2C convention
 ])
 def test_supported_codes(df, kw, span, buckets, code):
     assert df.supported(_shape(df, **kw), span, buckets) == code
@@ -86,6 +88,9 @@ def test_workspace_sizes(df):
     expect = [2 * (2 * L - 1) * 4, (2 * L - 1 + 2 * 256) * 4, H * T * R * 2, H * T * R * 2, 4 * H * T * 2]
     assert w0 == sum((x + 255) // 256 * 256 for x in expect)
     assert df.workspace_size(2, s, 512, 256) == 0
+    # the shared P2C convention adds the reversed q_r [H][R][D]
+    sh = _shape(df, p2c_convention=1)
+    assert df.workspace_size(0, sh, 512, 256) == w0 + (H * R * 64 * 2 + 255) // 256 * 256
     assert df.workspace_size(0, _shape(df, head_dim=48), 512, 256) == 0
 
 

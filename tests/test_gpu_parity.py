@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from synth import make_inputs, workload_inputs
-from parity_util import run_gpu, run_oracle, compare
+from parity_util import run_gpu, run_oracle, compare, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,27 @@ def test_parity_small(name):
     errs, bad = compare(inp, gpu, ref)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert not bad, f"{name}: {bad}"
+
+
+# the shared P2C convention (P2C takes the row C2P uses): the kernels run on
+# a reversed q_r with a reversed-coordinate table; the oracle indexes directly
+@pytest.mark.parametrize("name", ["bf16_D64_bucketed_ragged", "fp32_D64", "bf16_packed_masked",
+                                  "fp16_D128_unbucketed", "bf16_big_bucket_odd", "bf16_metric_index_L1024"])
+def test_parity_shared_p2c(name):
+    kw = CASES[name]
+    print(f"shared p2c case {name}: {kw}", flush=True)
+    inp = _inp(**kw)
+    gpu = run_gpu(inp, p2c="shared")
+    ref = run_oracle(inp, p2c="shared")
+    errs, bad = compare(inp, gpu, ref)
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert not bad, f"{name}: {bad}"
+    # the two conventions differ most in dk and dq_r (rel-L2 ~1 between the
+    # oracle's two results on these inputs): the GPU must be far from the
+    # literal ones
+    lit = run_oracle(inp)
+    for n in ("dk", "dq_r"):
+        assert rel_l2(gpu[n], lit[n]) > 0.2, n
 
 
 def test_workload1_forward():
