@@ -108,7 +108,7 @@ int check_all(const df_attn_shape* s, int32_t span, int32_t buckets, bool packed
 
 // Workspace plan. Offsets are relative to the workspace base.
 struct Plan {
-  size_t lut, lutp, qr_rev, c2ps, p2cs, ends, delta, dq_acc, dk_acc, dc2p, dp2c, part, total;
+  size_t lut, lutp, qr_rev, c2ps, p2cs, ends, delta, krT, qrT, dc2p, dp2c, part, total;
   int RP, nchunk, chunk_tokens;
 };
 
@@ -145,8 +145,8 @@ Plan make_plan(int pass, const df_attn_shape* s, int R) {
     pl.nchunk = int(nchunk);
     pl.chunk_tokens = int(ct);
     pl.delta = take(H * T * sizeof(float));
-    pl.dq_acc = take(H * T * D * sizeof(float));
-    pl.dk_acc = take(H * T * D * sizeof(float));
+    pl.krT = take(H * D * size_t(pl.RP) * es);
+    pl.qrT = take(H * D * size_t(pl.RP) * es);
     pl.dc2p = take(H * T * pl.RP * es);
     pl.dp2c = take(H * T * pl.RP * es);
     pl.part = take(2 * H * size_t(nchunk) * size_t(R) * D * sizeof(float));
@@ -473,21 +473,29 @@ int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   p.dqr = dq_r;
   p.dkr = dk_r;
   p.delta = reinterpret_cast<float*>(ws + pl.delta);
-  p.dq_acc = reinterpret_cast<float*>(ws + pl.dq_acc);
-  p.dk_acc = reinterpret_cast<float*>(ws + pl.dk_acc);
+  p.krT = ws + pl.krT;
+  p.qrT = ws + pl.qrT;
   p.dc2p = ws + pl.dc2p;
   p.dp2c = ws + pl.dp2c;
   p.part = reinterpret_cast<float*>(ws + pl.part);
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T > 0) {
+    // index tables (and the reversed q_r of the shared P2C convention), then
+    // the relative rows transposed for the dQ and dK/dV epilogues
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
-                       [&] { return launch_index(p, span, buckets, (char*)workspace, pl, st); })) ||
+                       [&] {
+                         hipError_t e = launch_index(p, span, buckets, ws, pl, st);
+                         const int es = p.dtype == dfa::DF_FP32_T ? 4 : 2;
+                         if (e == hipSuccess)
+                           e = dfa::launch_transpose_rows(p.kr, ws + pl.krT, p.H, p.R, p.RP, p.D, es, st);
+                         if (e == hipSuccess)
+                           e = dfa::launch_transpose_rows(p.qr, ws + pl.qrT, p.H, p.R, p.RP, p.D, es, st);
+                         return e;
+                       })) ||
         (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
         (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||
         (rc = run_stage(DF_STAGE_DQ, st, "dq kernel", [&] { return dfa::launch_bwd_dq(p, st); })) ||
-        (rc = run_stage(DF_STAGE_RELGRAD_DX, st, "relative gradient kernel",
-                        [&] { return dfa::launch_relgrad_dx(p, st); })) ||
         (rc = run_stage(DF_STAGE_RELGRAD_DW, st, "relative gradient kernel",
                         [&] { return dfa::launch_relgrad_dw(p, st); })))
       return rc;

@@ -356,18 +356,22 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     __syncthreads();
   }
 
+  // close this key's dP2C row, then add the relative term dP2C Q_r (the
+  // wave's rows are complete once its own stores are)
+  if (jin && g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
+  wait_vmem();
+  rel_epilogue<TR, ND>(dKt, wview, wbase, buf_view((const T*)p.qrT + int64_t(h) * D * RP, uint32_t(D * RP * ES)), RP);
   if (!jin) return;
   T* dvp = (T*)p.dv + tok_j * p.ts + int64_t(h) * p.hs;
-  float* dkp = p.dk_acc + (int64_t(h) * T_ + tok_j) * D;
+  T* dkp = (T*)p.dk + tok_j * p.ts + int64_t(h) * p.hs;
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int c = 32 * nd + acc_row(v, g);
       dvp[c] = TR::from_f(dVt[nd][v]);
-      dkp[c] = dKt[nd][v] * p.scale;
+      dkp[c] = TR::from_f(dKt[nd][v] * p.scale);
     }
-  if (g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
 }
 
 template <int DT, int D, bool NARROW>

@@ -298,13 +298,18 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     __syncthreads();
   }
 
+  // close this query's dC2P row, then add the relative term dC2P K_r: the
+  // wave's rows are complete once its own stores are (no other wave writes
+  // them, and no cache above L2 holds them)
+  if (qin && g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
+  wait_vmem();
+  rel_epilogue<TR, ND>(dQt, wview, wbase, buf_view((const T*)p.krT + int64_t(h) * D * RP, uint32_t(D * RP * ES)), RP);
   if (!qin) return;
-  float* dqp = p.dq_acc + (int64_t(h) * T_ + tok_i) * D;
+  T* dqp = (T*)p.dq + tok_i * p.ts + int64_t(h) * p.hs;
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dqp[32 * nd + acc_row(v, g)] = dQt[nd][v] * p.scale;
-  if (g == 0) walk_finish<TR>(wrow, R, RP, rc, sc);
+    for (int v = 0; v < 16; ++v) dqp[32 * nd + acc_row(v, g)] = TR::from_f(dQt[nd][v] * p.scale);
 }
 
 template <int DT, int D, bool NARROW>

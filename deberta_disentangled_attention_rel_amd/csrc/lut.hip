@@ -134,4 +134,29 @@ hipError_t launch_reverse_rows(const void* src, void* dst, int H, int R, int D, 
   return hipGetLastError();
 }
 
+// dst[h][d][r] = src[h][r][d] for r < R, 0 for R <= r < RP (the relative
+// rows transposed for the backward kernels' epilogue).
+namespace {
+template <typename T>
+__global__ void transpose_rows_kernel(const T* __restrict__ src, T* __restrict__ dst, int H, int R, int RP, int D) {
+  const int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (n >= int64_t(H) * D * RP) return;
+  const int64_t r = n % RP, hd = n / RP;
+  const int64_t d = hd % D, h = hd / D;
+  dst[n] = r < R ? src[(h * R + r) * D + d] : T(0);
+}
+}  // namespace
+
+hipError_t launch_transpose_rows(const void* src, void* dst, int H, int R, int RP, int D, int elem_bytes,
+                                 hipStream_t st) {
+  const int64_t total = int64_t(H) * D * RP;
+  if (total == 0) return hipSuccess;
+  const unsigned nb = unsigned((total + 255) / 256);
+  if (elem_bytes == 4)
+    transpose_rows_kernel<uint32_t><<<nb, 256, 0, st>>>((const uint32_t*)src, (uint32_t*)dst, H, R, RP, D);
+  else
+    transpose_rows_kernel<uint16_t><<<nb, 256, 0, st>>>((const uint16_t*)src, (uint16_t*)dst, H, R, RP, D);
+  return hipGetLastError();
+}
+
 }  // namespace dfa

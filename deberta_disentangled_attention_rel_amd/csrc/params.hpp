@@ -49,8 +49,8 @@ struct Params {
   void* ends;               // [4][H][T] dtype: c2ps[..][0], c2ps[..][R-1],
                             //   p2cs[..][0], p2cs[..][R-1]
   float* delta;             // [H][T]: rowsum(dO * O)
-  float* dq_acc;            // [H][T][D]: s * dS K
-  float* dk_acc;            // [H][T][D]: s * dS^T Q
+  const void* krT;          // [H][D][RP] dtype: k_r transposed (columns >= R zero)
+  const void* qrT;          // [H][D][RP] dtype: the q_r the kernels read, transposed
   void* dc2p;               // [H][T][RP] dtype: segmented sums of dS over delta(i,j)
   void* dp2c;               // [H][T][RP] dtype: segmented sums of dS over delta(j,i)
   float* part;              // [2][H][nchunk][R][D] split-K partials
@@ -82,12 +82,13 @@ struct ProjParams {
 hipError_t launch_lut(int Lmax, int span, int buckets, int p2c_shared, int32_t* c2p, int32_t* p2c, uint32_t* packed,
                       hipStream_t st);  // packed may be null
 hipError_t launch_reverse_rows(const void* src, void* dst, int H, int R, int D, int elem_bytes, hipStream_t st);
+hipError_t launch_transpose_rows(const void* src, void* dst, int H, int R, int RP, int D, int elem_bytes,
+                                 hipStream_t st);  // [H][R][D] -> [H][D][RP], zero columns >= R
 hipError_t launch_strips(const Params& p, hipStream_t st);  // both strips
 hipError_t launch_fwd(const Params& p, hipStream_t st);
 hipError_t launch_bwd_pre(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dkv(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq(const Params& p, hipStream_t st);
-hipError_t launch_relgrad_dx(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_dw(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_sum(const Params& p, hipStream_t st);
 hipError_t launch_proj(const ProjParams& p, hipStream_t st);

@@ -3,146 +3,22 @@
 // projections stay in the autograd graph; "Performance": the 12LRD term of
 // the backward count).
 //
-//   dq   = dq_acc + s * dC2P K_r      dk   = dk_acc + s * dP2C Q_r      (per token)
 //   dk_r = s * sum_t dC2P[t]^T Q[t]    dq_r = s * sum_t dP2C[t]^T K[t]    (per head)
 //
-// Both GEMMs stage row-major tiles with coalesced 16-byte loads, prefetching
-// the next tile into registers while the current one is multiplied (double-
-// buffered LDS, one barrier per step); operands that run down the rows are
-// read with transposing LDS reads. The token sums
-// are split into fixed chunks; each chunk's [R, D] partial is written to the
-// workspace and a second kernel adds the chunks in index order. No atomics;
-// the chunking depends only on the shape.
+// (The per-token terms s * dC2P K_r and s * dP2C Q_r are added by the dQ and
+// dK/dV kernels themselves, at the end of each work-group.) The GEMM stages
+// row-major tiles with coalesced 16-byte loads, prefetching the next tile
+// into registers while the current one is multiplied (double-buffered LDS,
+// one barrier per step); operands that run down the rows are read with
+// transposing LDS reads. The token sums are split into fixed chunks; each
+// chunk's [R, D] partial is written to the workspace and a second kernel adds
+// the chunks in index order. No atomics; the chunking depends only on the
+// shape.
 #include "pipe.hpp"
 
 namespace dfa {
 
 namespace {
-
-// Pieces of dx_kernel (see there). A chunk c of the strip rows (RC columns
-// of the work-group's rows) and of the relative rows (RC rows of D), as
-// range-checked 16-byte loads issued without a branch.
-template <typename T, int RC, int D, int GN, int WN>
-__device__ __forceinline__ void dx_load(uint4 (&g)[GN], uint4 (&w)[WN], BufView gv, BufView wv, int c, int nch,
-                                        int RP) {
-  constexpr int ES = int(sizeof(T)), CH = 16 / ES;
-  const int tid = threadIdx.x;
-  const bool live = c < nch;
-#pragma unroll
-  for (int u = 0; u < GN; ++u) {
-    const int it = tid + u * 256, row = it / (RC / CH), col = c * RC + (it % (RC / CH)) * CH;
-    g[u] = buf_load16(gv, live && col < RP ? (row * RP + col) * ES : kBufSkip);
-  }
-#pragma unroll
-  for (int u = 0; u < WN; ++u) {
-    const int it = tid + u * 256, row = c * RC + it / (D / CH), col = (it % (D / CH)) * CH;
-    w[u] = buf_load16(wv, live ? (row * D + col) * ES : kBufSkip);
-  }
-}
-template <typename T>
-__device__ __forceinline__ void dx_put(T* d, uint4 v) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint4*>(d) = v;
-  } else {
-    const float* f = reinterpret_cast<const float*>(&v);
-    d[0] = f[0];
-    d[1] = f[1];
-    d[2] = f[2];
-    d[3] = f[3];
-  }
-}
-template <typename T, int RC, int D, int GN, int WN, int GP, int WP>
-__device__ __forceinline__ void dx_store(const uint4 (&g)[GN], const uint4 (&w)[WN], T* gs, T* ws) {
-  constexpr int CH = 16 / int(sizeof(T));
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < GN; ++u) {
-    const int it = tid + u * 256;
-    dx_put(gs + (it / (RC / CH)) * GP + (it % (RC / CH)) * CH, g[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < WN; ++u) {
-    const int it = tid + u * 256;
-    dx_put(ws + (it / (D / CH)) * WP + (it % (D / CH)) * CH, w[u]);
-  }
-}
-template <typename TR, int RC, int ND, int GP, int WP>
-__device__ __forceinline__ void dx_mma(f32x16 (&acc)[ND], const typename TR::T* gs, const typename TR::T* ws, int row) {
-#pragma unroll
-  for (int q = 0; q < RC / TR::KS; ++q) {
-    const auto a = ld_row_fed<TR>(gs, GP, row, 0, q);
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(ws, WP, 0, 32 * nd, q), acc[nd]);
-  }
-}
-
-// which = 0: dC2P with K_r into dq; which = 1: dP2C with Q_r into dk.
-// Workgroup: 128 tokens (4 waves x 32) x all D columns, R in chunks of 64.
-// Two chunks are in flight in registers while a third is multiplied from LDS
-// (double-buffered, one barrier per chunk). Every load is a range-checked
-// buffer load issued without a branch (rows past T or R and columns past RP
-// read zero, chunks past the end load nothing), so waiting for the older
-// chunk never waits for the newer one.
-template <int DT, int D>
-__global__ __launch_bounds__(256) void dx_kernel(Params p) {
-  using TR = Tr<DT>;
-  using T = typename TR::T;
-  constexpr int KS = TR::KS, ND = D / 32, ES = int(sizeof(T)), CH = 16 / ES;
-  constexpr int TM = 128, RC = 64;
-  constexpr int GP = RowPitch<T, RC>::rows, WP = RowPitch<T, D>::cols;
-  constexpr int GN = TM * RC / CH / 256, WN = RC * D / CH / 256;  // 16-byte chunks per thread
-  static_assert(GN * CH * 256 == TM * RC && WN * CH * 256 == RC * D, "whole chunks per thread");
-  __shared__ __align__(16) T Gs[2][TM * GP];
-  __shared__ __align__(16) T Ws[2][RC * WP];
-
-  const int which = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, li = lane & 31, wave = tid >> 6;
-  const int h = blockIdx.y;
-  const int64_t t0 = int64_t(blockIdx.x) * TM;
-  const int R = p.R, RP = p.RP;
-  const T* G = (const T*)(which ? p.dp2c : p.dc2p) + (int64_t(h) * p.T + t0) * RP;
-  const T* W = (const T*)(which ? p.qr : p.kr) + int64_t(h) * R * D;
-  const float* acc_in = (which ? p.dk_acc : p.dq_acc) + int64_t(h) * p.T * D;
-  T* outp = (T*)(which ? p.dk : p.dq);
-  const int nt = int(min<int64_t>(TM, p.T - t0));
-  const BufView gv = buf_view(G, uint32_t(nt) * uint32_t(RP) * ES);
-  const BufView wv = buf_view(W, uint32_t(R) * D * ES);
-  const int nch = (R + RC - 1) / RC;
-
-  uint4 ga[GN], wa[WN], gb[GN], wb[WN];
-  f32x16 acc[ND];
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
-
-  dx_load<T, RC, D, GN, WN>(ga, wa, gv, wv, 0, nch, RP);
-  dx_store<T, RC, D, GN, WN, GP, WP>(ga, wa, Gs[0], Ws[0]);
-  __syncthreads();
-  dx_load<T, RC, D, GN, WN>(ga, wa, gv, wv, 1, nch, RP);
-  dx_load<T, RC, D, GN, WN>(gb, wb, gv, wv, 2, nch, RP);
-  for (int c = 0; c < nch; c += 2) {
-    // LDS buffer 0 holds chunk c, (ga, wa) chunk c + 1, (gb, wb) chunk c + 2
-    dx_mma<TR, RC, ND, GP, WP>(acc, Gs[0], Ws[0], wave * 32 + li);
-    dx_store<T, RC, D, GN, WN, GP, WP>(ga, wa, Gs[1], Ws[1]);
-    __syncthreads();
-    dx_load<T, RC, D, GN, WN>(ga, wa, gv, wv, c + 3, nch, RP);
-    if (c + 1 >= nch) break;
-    dx_mma<TR, RC, ND, GP, WP>(acc, Gs[1], Ws[1], wave * 32 + li);
-    dx_store<T, RC, D, GN, WN, GP, WP>(gb, wb, Gs[0], Ws[0]);
-    __syncthreads();
-    dx_load<T, RC, D, GN, WN>(gb, wb, gv, wv, c + 4, nch, RP);
-  }
-  // C[m = token][n = d]: lane holds column d = 32nd + li, rows acc_row(v, g)
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t t = t0 + wave * 32 + acc_row(v, g);
-      if (t >= p.T) continue;
-      const int c = 32 * nd + li;
-      const float val = acc_in[t * D + c] + p.scale * acc[nd][v];
-      outp[t * p.ts + int64_t(h) * p.hs + c] = TR::from_f(val);
-    }
-}
 
 // Split-K partials of dk_r (which = 0: dC2P^T Q) and dq_r (which = 1: dP2C^T K).
 // Workgroup: 128 strip rows r (4 waves x 32) x all D columns, over one chunk
@@ -231,12 +107,6 @@ __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
 }
 
 template <int DT, int D>
-void launch_dx_d(const Params& p, hipStream_t st) {
-  dim3 g1(unsigned((p.T + 127) / 128), unsigned(p.H), 2u);
-  dx_kernel<DT, D><<<g1, 256, 0, st>>>(p);
-}
-
-template <int DT, int D>
 void launch_dw_d(const Params& p, hipStream_t st) {
   dim3 g2(unsigned((p.R + 127) / 128), unsigned(p.nchunk), unsigned(2 * p.H));
   dw_kernel<DT, D><<<g2, 256, 0, st>>>(p);
@@ -268,12 +138,6 @@ void launch_sum_dt(const Params& p, hipStream_t st) {
   }
 
 }  // namespace
-
-hipError_t launch_relgrad_dx(const Params& p, hipStream_t st) {
-  if (p.T == 0) return hipSuccess;
-  DF_DISPATCH(launch_dx_d, p, st)
-  return hipGetLastError();
-}
 
 hipError_t launch_relgrad_dw(const Params& p, hipStream_t st) {
   if (p.T == 0) return hipSuccess;

@@ -195,4 +195,43 @@ struct StripWalk {
 __device__ __forceinline__ constexpr int walk_grp(int k) { return (k >> 2) & 1; }
 __device__ __forceinline__ constexpr int walk_reg(int k) { return 4 * (k >> 3) + (k & 3); }
 
+// Relative-gradient epilogue of the dQ and dK/dV kernels:
+//   acc[nd] += relT[32 nd + m][:] . strip[partner][:]
+// for the accumulator tiles of a lane's partner (column = this lane's query
+// or key, rows m = acc_row(v, g) of d-block nd): dQ^T += K_r^T dC2P^T and
+// dK^T += Q_r^T dP2C^T. `rows` views the work-group's strip rows (`row_off`:
+// byte offset of this lane's partner row; partners past the sequence read
+// zero), `relT` the head's relative rows transposed, [D][RP]. Chunks at or
+// past RP are skipped (they would run into the next row). The strip rows
+// must be complete and visible: every lane that wrote them has waited for
+// its stores.
+template <typename TR, int ND>
+__device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, int row_off, BufView relT, int RP) {
+  using frag = typename TR::frag;
+  constexpr int E = TR::E, KS = TR::KS, ES = int(sizeof(typename TR::T));
+  constexpr int U = 16;  // contraction steps with their loads in flight together
+  const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
+  auto ld = [&](BufView v, int off) -> frag {
+    if constexpr (E == 8)
+      return __builtin_bit_cast(frag, buf_load16(v, off));
+    else
+      return buf_load<typename TR::T>(v, off, 0);
+  };
+  for (int r0 = 0; r0 < RP; r0 += U * KS) {
+    frag b[U], a[U][ND];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * KS + g * E;
+      const bool in = r < RP;
+      b[u] = ld(rows, in ? row_off + r * ES : kBufSkip);
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) a[u][nd] = ld(relT, in ? ((32 * nd + li) * RP + r) * ES : kBufSkip);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a[u][nd], b[u], acc[nd]);
+  }
+}
+
 }  // namespace dfa

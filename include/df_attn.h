@@ -248,8 +248,10 @@ const char* df_last_error(void);
  * Not thread-safe; meant for a single benchmarking thread. */
 enum {
   DF_STAGE_INDEX = 0, DF_STAGE_STRIPS = 1, DF_STAGE_FWD = 2, DF_STAGE_DELTA = 3,
-  DF_STAGE_DKV = 4, DF_STAGE_DQ = 5, DF_STAGE_RELGRAD_DX = 6, DF_STAGE_RELGRAD_DW = 7,
-  DF_STAGE_RELGRAD_SUM = 8, DF_NUM_STAGES = 9
+  DF_STAGE_DKV = 4, DF_STAGE_DQ = 5,
+  DF_STAGE_RELGRAD_DX = 6, /* not launched: the dQ and dK/dV kernels add the per-token
+                              relative terms themselves */
+  DF_STAGE_RELGRAD_DW = 7, DF_STAGE_RELGRAD_SUM = 8, DF_NUM_STAGES = 9
 };
 int df_attn_profile_enable(int on);
 int df_attn_profile_read(float* ms, int* launches, int n_stages);
