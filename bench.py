@@ -43,13 +43,13 @@ def flops_fwd_bwd(B, H, L, D, R):
 def kernel_algorithmic_flops(stage, B, H, L, D, R):
     """Algorithmic FLOPs of one launch of a stage (matrix products it must run)."""
     per = B * H * L * L * D
+    rel = B * H * L * R * D
     return {
-        "fwd": 4.0 * per,            # S = QK^T, O = PV
-        "bwd_dkv": 8.0 * per,        # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
-        "bwd_dq": 6.0 * per,         # S, dP, dQ = dS K
-        "strips": 2.0 * B * H * L * R * D,       # one of Q K_r^T / K Q_r^T
-        "relgrad_dx": 4.0 * B * H * L * R * D,   # dC2P K_r and dP2C Q_r
-        "relgrad_dw": 4.0 * B * H * L * R * D,   # dC2P^T Q and dP2C^T K
+        "fwd": 4.0 * per,                  # S = QK^T, O = PV
+        "bwd_dkv": 8.0 * per + 2.0 * rel,  # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dP2C Q_r
+        "bwd_dq": 6.0 * per + 2.0 * rel,   # S, dP, dQ = dS K; dC2P K_r
+        "strips": 2.0 * rel,               # one of Q K_r^T / K Q_r^T
+        "relgrad_dw": 4.0 * rel,           # dC2P^T Q and dP2C^T K
     }.get(stage)
 
 
