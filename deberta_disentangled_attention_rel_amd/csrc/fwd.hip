@@ -35,6 +35,8 @@ namespace dfa {
 
 namespace {
 
+constexpr float kMaxSlack = 8.f;
+
 template <int DT, int D, int NKT, bool NARROW, bool DROP>
 __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd_kernel(Params p) {
   using TR = Tr<DT>;
@@ -277,7 +279,12 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
 #pragma unroll
         for (int v = 0; v < 16; ++v) mt = fmaxf(mt, y[t][v]);
       mt = fmaxf(mt, xor32(mt)) + a;
-      const float mnew = fmaxf(m, mt);
+      // the running max moves only when the tile's max exceeds it by more
+      // than kMaxSlack (log2 units): otherwise the probabilities are taken
+      // against the old max (at most 2^kMaxSlack, exact in fp32 sums and at
+      // full relative precision in the 16-bit P operand) and O needs no
+      // rescale; O / l and the LSE are the same either way
+      const float mnew = mt > m + kMaxSlack ? mt : m;
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
       const float m_old = m;
       const float shift = msafe - a;
