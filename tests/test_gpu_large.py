@@ -20,11 +20,11 @@ from parity_util import rel_l2, TOL, to_dev
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _gpu(inp, backward):
+def _gpu(inp, backward, p2c="literal"):
     import deberta_disentangled_attention_rel_amd as df
     w = inp.workload
     t, km, cu = to_dev(inp)
-    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen, p2c=p2c)
     out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
     res = {"out": out, "lse": lse}
     if backward:
@@ -35,17 +35,17 @@ def _gpu(inp, backward):
     return {k: v.float().cpu().numpy() for k, v in res.items()}
 
 
-def _check(n, dtype=None, backward=True):
+def _check(n, dtype=None, backward=True, p2c="literal"):
     inp = workload_inputs(n, dtype=dtype, with_dout=backward)
     w = inp.workload
-    print(f"workload {n} ({w.name}, {inp.dtype}): T={inp.total_tokens} nseq={inp.nseq}", flush=True)
-    gpu = _gpu(inp, backward)
+    print(f"workload {n} ({w.name}, {inp.dtype}, p2c {p2c}): T={inp.total_tokens} nseq={inp.nseq}", flush=True)
+    gpu = _gpu(inp, backward, p2c)
     f = inp.f64
     H = w.heads
     rng = np.random.default_rng(w.seed + 1)
     full = sorted(rng.choice(H, size=min(2, H), replace=False).tolist())
     tol_f, tol_b = TOL[inp.dtype]
-    kw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq)
+    kw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq, p2c=p2c)
     out, lse = oracle.forward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], w.span, w.buckets,
                               heads=full, **kw)
     errs = {}
@@ -74,12 +74,12 @@ def _check(n, dtype=None, backward=True):
                 continue
             rows = np.array([int(rng.integers(en - st))])
             o, l = oracle.forward_rows(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], w.span,
-                                       w.buckets, (st, en), h, rows, key_mask=inp.key_mask)
+                                       w.buckets, (st, en), h, rows, key_mask=inp.key_mask, p2c=p2c)
             go.append(gpu["out"][st + rows, h]); ro.append(o)
             gl.append(gpu["lse"][h, st + rows]); rl.append(l)
             if backward:
                 d = oracle.dq_rows(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], f["dout"], w.span,
-                                   w.buckets, (st, en), h, rows, key_mask=inp.key_mask)
+                                   w.buckets, (st, en), h, rows, key_mask=inp.key_mask, p2c=p2c)
                 gq.append(gpu["dq"][st + rows, h]); rq.append(d)
     if rest:
         gl_, rl_ = np.concatenate(gl), np.concatenate(rl)
@@ -105,6 +105,12 @@ def test_workload3_bf16_L8192_fwd_bwd():
 
 def test_workload4_packed_varlen_masked():
     _check(4)
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_shared_p2c_full_size(n):
+    """The shared P2C convention at the L=8192 and packed workloads."""
+    _check(n, p2c="shared")
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "fp32"])
