@@ -8,8 +8,11 @@ position_buckets=256, max_relative_positions=512 (R=512), synthetic seeded
 inputs N(0, 1/D), dout N(0, 1).
 
 A step is one pass of the whole path: the forward (index tables, strips,
-fused forward) and the backward (index tables, strips, Delta, dK/dV, dQ,
-relative-gradient GEMMs). FLOPs per step follow the page's convention,
+fused forward) and the backward (Delta, dK/dV and dQ with their
+relative-gradient epilogues, the split-K relative-row gradients), which
+reuses the forward's index tables and strips from the shared workspace
+(DF_FLAG_BWD_REUSE_FWD; the line also reports the backward recomputing
+them). FLOPs per step follow the page's convention,
 B*H*(14 L^2 D + 16 L R D). Inputs, outputs and the workspace are resident in
 HBM before timing; nothing is allocated inside the timed region.
 
@@ -165,7 +168,10 @@ def main(argv=None) -> int:
 
     def step():
         df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws)
-        df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads, workspace=ws)
+        # the backward reuses the forward's index tables and strips, which stay
+        # in the shared workspace (DF_FLAG_BWD_REUSE_FWD)
+        df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads, workspace=ws,
+               reuse_fwd_workspace=True)
 
     for _ in range(a.warmup):
         step()
@@ -203,7 +209,10 @@ def main(argv=None) -> int:
 
     fwd_ms = timed(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws), a.steps)
     bwd_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
-                                  workspace=ws), a.steps)
+                                  workspace=ws, reuse_fwd_workspace=True), a.steps)
+    # the backward on its own, recomputing the index tables and strips
+    bwd_recompute_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout,
+                                            grads=grads, workspace=ws), a.steps)
     # the inference forward (no LSE), into its own output buffer
     out_inf = torch.empty_like(out)
     inf_ms = timed(lambda: df.fwd_inference(q, k, v, q_r, k_r, w.span, w.buckets, out=out_inf, workspace=ws),
@@ -215,7 +224,7 @@ def main(argv=None) -> int:
         df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out_inf, lse=lse_d, workspace=ws,
                dropout_p=0.1, seed=1234, offset=0)
         df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out_inf, lse_d, dout, grads=grads, workspace=ws,
-               dropout_p=0.1, seed=1234, offset=0)
+               dropout_p=0.1, seed=1234, offset=0, reuse_fwd_workspace=True)
     drop_step()
     drop_ms = timed(drop_step, max(1, a.steps // 3))
 
@@ -269,6 +278,8 @@ def main(argv=None) -> int:
                     "median": round(pct(per_step, 0.5), 4), "p90": round(pct(per_step, 0.9), 4)},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "bwd_recompute_ms": round(bwd_recompute_ms, 4),
+        "bwd_reuses_fwd_strips": True,
         "inference_fwd_ms": round(inf_ms, 4),
         "dropout_0.1_step_ms": round(drop_ms, 4),
         "qkv_proj": {"ms": round(proj_ms, 4), "tflops": round(proj_flops / (proj_ms * 1e-3) / 1e12, 1),

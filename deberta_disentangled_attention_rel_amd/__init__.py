@@ -46,7 +46,7 @@ class Shape(ctypes.Structure):
                 ("total_tokens", ctypes.c_int64), ("num_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
-                ("p2c_convention", ctypes.c_int32)]
+                ("p2c_convention", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -131,14 +131,17 @@ def _as_thd(x: torch.Tensor) -> torch.Tensor:
 P2C_CONVENTIONS = {"literal": 0, "shared": 1}
 
 
-def make_shape(q: torch.Tensor, batch: int, max_seqlen: int, p2c: str = "literal") -> Shape:
+FLAG_BWD_REUSE_FWD = 1
+
+
+def make_shape(q: torch.Tensor, batch: int, max_seqlen: int, p2c: str = "literal", flags: int = 0) -> Shape:
     T, H, D = q.shape
     if q.dtype not in DTYPE_CODES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if p2c not in P2C_CONVENTIONS:
         raise ValueError(f"p2c must be one of {sorted(P2C_CONVENTIONS)}")
     return Shape(int(batch), int(max_seqlen), int(T), int(H), int(D), DTYPE_CODES[q.dtype],
-                 int(q.stride(0)), int(q.stride(1)), P2C_CONVENTIONS[p2c])
+                 int(q.stride(0)), int(q.stride(1)), P2C_CONVENTIONS[p2c], int(flags))
 
 
 def _layout(q, k, v, cu_seqlens, max_seqlen):
@@ -253,11 +256,17 @@ def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_
 
 def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=None,
         cu_seqlens=None, max_seqlen: Optional[int] = None, grads=None, workspace=None,
-        dropout_p: float = 0.0, seed: int = 0, offset: int = 0, p2c: str = "literal"):
+        dropout_p: float = 0.0, seed: int = 0, offset: int = 0, p2c: str = "literal",
+        reuse_fwd_workspace: bool = False):
     """Backward pass. Returns ``(dq, dk, dv, dq_r, dk_r)``. The dropout
-    arguments and ``p2c`` must be those of the forward that produced ``out``."""
+    arguments and ``p2c`` must be those of the forward that produced ``out``.
+    ``reuse_fwd_workspace``: ``workspace`` is the buffer that forward used
+    (sized for the backward) and still holds its index tables and strips
+    (DF_FLAG_BWD_REUSE_FWD)."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
-    shape = make_shape(q3, batch, L, p2c)
+    if reuse_fwd_workspace and workspace is None:
+        raise ValueError("reuse_fwd_workspace needs the forward's workspace")
+    shape = make_shape(q3, batch, L, p2c, FLAG_BWD_REUSE_FWD if reuse_fwd_workspace else 0)
     out3, dout3 = _as_thd(out).contiguous(), _as_thd(dout).contiguous()
     if grads is None:
         grads = (torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3),

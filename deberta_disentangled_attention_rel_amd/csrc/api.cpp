@@ -59,6 +59,8 @@ int check_shape(const df_attn_shape* s) {
   if (s->p2c_convention != DF_P2C_LITERAL && s->p2c_convention != DF_P2C_SHARED)
     return fail(DF_ERR_INVALID, "p2c_convention must be DF_P2C_LITERAL (0) or DF_P2C_SHARED (1), got %d",
                 s->p2c_convention);
+  if (s->flags & ~int32_t(DF_FLAG_BWD_REUSE_FWD))
+    return fail(DF_ERR_INVALID, "unknown flags 0x%x", unsigned(s->flags));
   if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
     return fail(DF_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128, got %d", s->head_dim);
   if (s->batch < 1) return fail(DF_ERR_INVALID, "batch must be >= 1, got %d", s->batch);
@@ -478,13 +480,20 @@ int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
   p.dc2p = ws + pl.dc2p;
   p.dp2c = ws + pl.dp2c;
   p.part = reinterpret_cast<float*>(ws + pl.part);
+  const bool reuse = (shape->flags & DF_FLAG_BWD_REUSE_FWD) != 0;
   if ((rc = set_dropout(p, drop))) return rc;
   if (p.T > 0) {
     // index tables (and the reversed q_r of the shared P2C convention), then
     // the relative rows transposed for the dQ and dK/dV epilogues
     if ((rc = run_stage(DF_STAGE_INDEX, st, "relative index kernel",
                        [&] {
-                         hipError_t e = launch_index(p, span, buckets, ws, pl, st);
+                         // with DF_FLAG_BWD_REUSE_FWD the forward's tables and strips
+                         // (and reversed q_r) are still in the workspace
+                         hipError_t e = hipSuccess;
+                         if (reuse)
+                           p.qr = p.p2c_shared ? static_cast<const void*>(ws + pl.qr_rev) : q_r;
+                         else
+                           e = launch_index(p, span, buckets, ws, pl, st);
                          const int es = p.dtype == dfa::DF_FP32_T ? 4 : 2;
                          if (e == hipSuccess)
                            e = dfa::launch_transpose_rows(p.kr, ws + pl.krT, p.H, p.R, p.RP, p.D, es, st);
@@ -492,7 +501,7 @@ int bwd_impl(const df_attn_shape* shape, const void* q, const void* k, const voi
                            e = dfa::launch_transpose_rows(p.qr, ws + pl.qrT, p.H, p.R, p.RP, p.D, es, st);
                          return e;
                        })) ||
-        (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); })) ||
+        (!reuse && (rc = run_stage(DF_STAGE_STRIPS, st, "strip kernel", [&] { return dfa::launch_strips(p, st); }))) ||
         (rc = run_stage(DF_STAGE_DELTA, st, "delta kernel", [&] { return dfa::launch_bwd_pre(p, st); })) ||
         (rc = run_stage(DF_STAGE_DKV, st, "dk/dv kernel", [&] { return dfa::launch_bwd_dkv(p, st); })) ||
         (rc = run_stage(DF_STAGE_DQ, st, "dq kernel", [&] { return dfa::launch_bwd_dq(p, st); })) ||

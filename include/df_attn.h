@@ -85,7 +85,17 @@ typedef struct {
   int64_t tok_stride;     /* element stride between tokens of [T,H,D] tensors */
   int64_t head_stride;    /* element stride between heads of [T,H,D] tensors */
   int32_t p2c_convention; /* DF_P2C_LITERAL (0) or DF_P2C_SHARED (1) */
+  int32_t flags;          /* 0 or DF_FLAG_BWD_REUSE_FWD */
 } df_attn_shape;
+
+/* df_attn_shape.flags. DF_FLAG_BWD_REUSE_FWD (df_attn_bwd only): the
+ * workspace still holds what the df_attn_fwd call with the same inputs,
+ * shape and index configuration left in it (the caller gave both calls the
+ * same buffer, of df_attn_workspace_size(1, ...) bytes, and nothing wrote to
+ * it in between); the backward then reuses that call's index tables and
+ * relative-position strips instead of recomputing them. The results are the
+ * same bit for bit; if the contents are not the forward's, they are wrong. */
+enum { DF_FLAG_BWD_REUSE_FWD = 1 };
 
 /* Non-raising eligibility check (the strict-contract idea of the
  * FastFlashAttention page, "Strict policy + fallback"). Returns DF_OK when

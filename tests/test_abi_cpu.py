@@ -73,6 +73,8 @@ def _shape(df, **kw):
     (dict(), 512, -2, 1),
     (dict(p2c_convention=1), 512, 256, 0),
     (dict(p2c_convention=2), 512, 256, 1),         # unknown P2C convention
+    (dict(flags=1), 512, 256, 0),
+    (dict(flags=2), 512, 256, 1),                  # unknown flag
 ])
 def test_supported_codes(df, kw, span, buckets, code):
     assert df.supported(_shape(df, **kw), span, buckets) == code

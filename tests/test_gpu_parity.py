@@ -99,6 +99,29 @@ def test_parity_shared_p2c(name):
         assert rel_l2(gpu[n], lit[n]) > 0.2, n
 
 
+@pytest.mark.parametrize("name,p2c", [("bf16_D64_bucketed_ragged", "literal"), ("fp32_D64", "literal"),
+                                      ("bf16_packed_masked", "shared")])
+def test_bwd_reuses_forward_workspace(name, p2c):
+    """DF_FLAG_BWD_REUSE_FWD: the backward on the forward's workspace (its
+    index tables and strips kept) equals the recomputing backward bit for bit."""
+    import deberta_disentangled_attention_rel_amd as df
+    from parity_util import to_dev
+    print(f"bwd reuse {name} {p2c}", flush=True)
+    inp = _inp(**CASES[name])
+    w = inp.workload
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen, p2c=p2c)
+    args = (t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets)
+    shape = df.make_shape(t["q"].view(-1, *t["q"].shape[-2:]), inp.nseq, inp.max_seqlen, p2c)
+    ws = torch.empty(df.workspace_size(1, shape, w.span, w.buckets), dtype=torch.uint8, device="cuda")
+    out, lse = df.fwd(*args, workspace=ws, **kw)
+    g_reuse = df.bwd(*args, out, lse, t["dout"], workspace=ws, reuse_fwd_workspace=True, **kw)
+    g_fresh = df.bwd(*args, out, lse, t["dout"], **kw)
+    torch.cuda.synchronize()
+    for n_, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g_reuse, g_fresh):
+        assert torch.equal(a, b), n_
+
+
 def test_workload1_forward():
     inp = workload_inputs(1)
     gpu = run_gpu(inp, backward=False)
