@@ -202,3 +202,22 @@ def test_dropout_parity(name):
     bad = {n_: e for n_, e in errs.items()
            if not np.isfinite(e) or e > (tol_f if n_ in ("out", "lse") else tol_b)}
     assert not bad, (errs, bad)
+
+
+# ----------------------------------------------------------------------------
+# structure the method fixes, checked on the GPU's own output: every valid row
+# of dS sums to zero, so sum_r dK_r[h, r, :] = 0 (up to the rounding of the
+# stored dC2P strip and of dk_r); sum_r dQ_r is not zero
+
+@pytest.mark.parametrize("name", ["bf16_D64_bucketed_ragged", "fp32_D64", "bf16_packed_masked"])
+def test_gpu_dk_r_rows_sum_to_zero(name):
+    inp = _inp(**CASES[name])
+    print(f"zero sums {name}", flush=True)
+    gpu = run_gpu(inp)
+    for h in range(gpu["dk_r"].shape[0]):
+        s_k = np.linalg.norm(gpu["dk_r"][h].astype(np.float64).sum(axis=0))
+        s_q = np.linalg.norm(gpu["dq_r"][h].astype(np.float64).sum(axis=0))
+        n_k = np.linalg.norm(gpu["dk_r"][h].astype(np.float64))
+        tol = 1e-5 if inp.dtype == "fp32" else 2e-2
+        assert s_k <= tol * n_k, (h, s_k, n_k)
+        assert s_q > 10 * tol * np.linalg.norm(gpu["dq_r"][h].astype(np.float64))
