@@ -150,7 +150,9 @@ int df_attn_fwd_inference(const df_attn_shape* shape,
 /* Backward pass: given the forward's out and lse and the output gradient
  * dout, writes dq, dk, dv [T,H,D] and dq_r, dk_r [H,R,D] (all dtype). The
  * gradients overwrite the outputs (never accumulate). Scores are recomputed
- * from the inputs and lse; nothing of the forward's workspace is reused. */
+ * from the inputs and lse; the index tables and relative-position strips are
+ * recomputed too, unless shape->flags has DF_FLAG_BWD_REUSE_FWD (then they
+ * are taken from the forward's workspace, see there). */
 int df_attn_bwd(const df_attn_shape* shape,
                 const void* q, const void* k, const void* v,
                 const void* q_r, const void* k_r,
