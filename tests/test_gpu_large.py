@@ -137,3 +137,36 @@ def test_inference_forward_full_size(n):
     out_i = df.fwd_inference(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out_i, out_t)
+
+
+def test_dropout_full_size_one_head():
+    """Attention dropout (p = 0.1) at the L=8192 workload: one seeded head in
+    full (both sequences, every output including that head's dq_r / dk_r),
+    which exercises the Philox counters at large query and key indices."""
+    import deberta_disentangled_attention_rel_amd as df
+    inp = workload_inputs(3)
+    w = inp.workload
+    p, seed, offset = 0.1, 20261203, 7
+    print(f"dropout full size p={p}", flush=True)
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen, dropout_p=p, seed=seed, offset=offset)
+    args = (t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets)
+    out, lse = df.fwd(*args, **kw)
+    g = df.bwd(*args, out, lse, t["dout"], **kw)
+    torch.cuda.synchronize()
+    h = int(np.random.default_rng(w.seed + 3).integers(w.heads))
+    f = inp.f64
+    okw = dict(key_mask=inp.key_mask, cu_seqlens=inp.cu_seqlens, batch=inp.nseq, heads=[h],
+               dropout=(p, seed, offset))
+    ro, rl = oracle.forward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], w.span, w.buckets, **okw)
+    rg = oracle.backward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], f["dout"], w.span, w.buckets, **okw)
+    tol_f, tol_b = TOL[inp.dtype]
+    errs = {"out": (rel_l2(out.float().cpu().numpy()[:, h], ro[:, h]), tol_f),
+            "lse": (rel_l2(lse.cpu().numpy()[h], rl[h]), tol_f)}
+    for name, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g, rg):
+        a = a.float().cpu().numpy()
+        errs[name] = (rel_l2(a[:, h] if name in ("dq", "dk", "dv") else a[h],
+                             b[:, h] if name in ("dq", "dk", "dv") else b[h]), tol_b)
+    print({k: f"{e:.2e}" for k, (e, _) in errs.items()}, flush=True)
+    bad = {k: e for k, (e, t_) in errs.items() if not (e <= t_)}
+    assert not bad, bad
