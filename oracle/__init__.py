@@ -10,5 +10,5 @@ from .df_oracle import (  # noqa: F401
     forward, backward, forward_rows, dq_rows,
 )
 from . import philox  # noqa: F401
-from .proj import qkv_projection  # noqa: F401
+from .proj import qkv_projection, qkv_projection_backward  # noqa: F401
 from .pack import pack_padded, unpack_packed  # noqa: F401

@@ -44,3 +44,31 @@ def qkv_projection(x, w, b, rel, H: int, D: int):
     q_r = yr[:, :HD].reshape(-1, H, D).transpose(1, 0, 2)   # [H, R, D]
     k_r = yr[:, HD:].reshape(-1, H, D).transpose(1, 0, 2)
     return q, k, v, q_r, k_r
+
+
+def qkv_projection_backward(x, w, rel, dq, dk, dv, dq_r, dk_r, H: int, D: int):
+    """Gradients of the projections above for output gradients dq, dk, dv
+    ``[T, H, D]`` and (with ``rel``) dq_r, dk_r ``[H, R, D]``: returns
+    (dx ``[T, E]``, dw ``[3 H D, E]``, db ``[3 H D]``, drel ``[R, E]`` or None),
+    float64. Each map is linear, so with dY the output gradients laid out like
+    the GEMM's output (``[T, 3 H D]``, and ``[R, 2 H D]`` for the relative
+    rows): dx = dY W, drel = dY_r W[:2HD], dW = dY^T x + [dY_r^T rel; 0],
+    db = column sums of dY and dY_r."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T = x.shape[0]
+    HD = H * D
+    dY = np.concatenate([np.asarray(g, dtype=np.float64).reshape(T, HD) for g in (dq, dk, dv)], axis=1)
+    dx = dY @ w
+    dw = dY.T @ x
+    db = dY.sum(axis=0)
+    drel = None
+    if rel is not None:
+        rel = np.asarray(rel, dtype=np.float64)
+        R = rel.shape[0]
+        dYr = np.concatenate([np.asarray(g, dtype=np.float64).transpose(1, 0, 2).reshape(R, HD)
+                              for g in (dq_r, dk_r)], axis=1)                    # [R, 2 H D]
+        drel = dYr @ w[:2 * HD]
+        dw[:2 * HD] += dYr.T @ rel
+        db[:2 * HD] += dYr.sum(axis=0)
+    return dx, dw, db, drel

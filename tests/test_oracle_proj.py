@@ -73,3 +73,44 @@ def test_relative_rows_are_projected_like_tokens():
     q, k, _, q_r, k_r = oracle.qkv_projection(rel, w, b, rel, H, D)
     np.testing.assert_allclose(q_r, q.transpose(1, 0, 2), rtol=0, atol=1e-13)
     np.testing.assert_allclose(k_r, k.transpose(1, 0, 2), rtol=0, atol=1e-13)
+
+
+def test_backward_finite_differences():
+    """The projection backward against central differences of the forward
+    oracle (the maps are linear in each argument, so the differences are
+    exact up to rounding)."""
+    rng = np.random.default_rng(9)
+    T, E, H, D, R = 4, 6, 2, 3, 5
+    HD = H * D
+    x, w, b, rel = _rand(rng, T, E), _rand(rng, 3 * HD, E), _rand(rng, 3 * HD), _rand(rng, R, E)
+    G = [_rand(rng, T, H, D) for _ in range(3)] + [_rand(rng, H, R, D) for _ in range(2)]
+
+    def loss(x_, w_, b_, rel_):
+        outs = oracle.qkv_projection(x_, w_, b_, rel_, H, D)
+        return sum(float((o * g).sum()) for o, g in zip(outs, G))
+
+    dx, dw, db, drel = oracle.qkv_projection_backward(x, w, rel, *G, H, D)
+    eps = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (b, db), (rel, drel)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss(x, w, b, rel)
+            arr[idx] = old - eps
+            lm = loss(x, w, b, rel)
+            arr[idx] = old
+            assert abs((lp - lm) / (2 * eps) - grad[idx]) <= 1e-6 * (1 + abs(grad[idx]))
+
+
+def test_backward_without_relative_rows():
+    rng = np.random.default_rng(10)
+    T, E, H, D = 3, 4, 1, 2
+    x, w = _rand(rng, T, E), _rand(rng, 3 * H * D, E)
+    G = [_rand(rng, T, H, D) for _ in range(3)]
+    dx, dw, db, drel = oracle.qkv_projection_backward(x, w, None, *G, None, None, H, D)
+    assert drel is None
+    dY = np.concatenate([g.reshape(T, -1) for g in G], axis=1)
+    for t in range(T):
+        for e in range(E):
+            assert abs(dx[t, e] - sum(dY[t, n] * w[n, e] for n in range(3 * H * D))) < 1e-12
+    np.testing.assert_allclose(db, dY.sum(axis=0), rtol=0, atol=1e-12)
