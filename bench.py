@@ -237,7 +237,15 @@ def main(argv=None) -> int:
     pouts = df.qkv_proj(pt["x"], pt["w"], pt["bias"], pt["rel"], H, D)
     proj_ms = timed(lambda: df.qkv_proj(pt["x"], pt["w"], pt["bias"], pt["rel"], H, D, out=pouts), a.steps)
     proj_flops = 2.0 * B * L * (H * D) * 3 * H * D + 2.0 * R * (H * D) * 2 * H * D
-    del pt, pouts
+    # and its backward (dx, dW, db, d_rel) for unit output gradients
+    pg = torch.ones((B * L, 3, H, D), dtype=torch.bfloat16, device=dev)
+    pr = torch.ones((H, R, D), dtype=torch.bfloat16, device=dev)
+    pws = torch.empty(df.lib().df_qkv_proj_bwd_workspace_size(B * L, H * D, H, D, R, 0), dtype=torch.uint8,
+                      device=dev)
+    df.qkv_proj_bwd(pt["x"], pt["w"], pt["rel"], pg, pr, pr, H, D, workspace=pws)
+    proj_bwd_ms = timed(lambda: df.qkv_proj_bwd(pt["x"], pt["w"], pt["rel"], pg, pr, pr, H, D, workspace=pws),
+                        a.steps)
+    del pt, pouts, pg, pr, pws
 
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
@@ -283,6 +291,8 @@ def main(argv=None) -> int:
         "inference_fwd_ms": round(inf_ms, 4),
         "dropout_0.1_step_ms": round(drop_ms, 4),
         "qkv_proj": {"ms": round(proj_ms, 4), "tflops": round(proj_flops / (proj_ms * 1e-3) / 1e12, 1),
+                     "bwd_ms": round(proj_bwd_ms, 4),
+                     "bwd_tflops": round(2 * proj_flops / (proj_bwd_ms * 1e-3) / 1e12, 1),
                      "shape": f"x [{B * L}, {H * D}] w [{3 * H * D}, {H * D}] rel [{R}, {H * D}]"},
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(dom_tf, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",

@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "fwd_inference", "bwd",
-           "qkv_proj", "pack_padded", "unpack_packed",
+           "qkv_proj", "qkv_proj_bwd", "pack_padded", "unpack_packed",
            "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdf_attn.so")
@@ -29,7 +29,7 @@ EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
             "df_attn_bwd_dropout", "df_strerror", "df_last_error",
             "df_attn_version",
             "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name", "df_qkv_proj",
-            "df_pack_padded", "df_unpack_packed")
+            "df_pack_padded", "df_unpack_packed", "df_qkv_proj_bwd", "df_qkv_proj_bwd_workspace_size")
 NUM_STAGES = 9
 
 
@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.df_attn_bwd.restype = ctypes.c_int
     L.df_qkv_proj.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.df_qkv_proj.restype = ctypes.c_int
+    L.df_qkv_proj_bwd_workspace_size.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32]
+    L.df_qkv_proj_bwd_workspace_size.restype = ctypes.c_size_t
+    L.df_qkv_proj_bwd.argtypes = [ctypes.c_int64, i32, i32, i32, i32, i32] + [vp] * 10 + [vp, sz, vp]
+    L.df_qkv_proj_bwd.restype = ctypes.c_int
     L.df_pack_padded.argtypes = [i32, i32, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
     L.df_pack_padded.restype = ctypes.c_int
     L.df_unpack_packed.argtypes = [i32, i32, ctypes.c_int64, vp, vp, vp, vp, vp]
@@ -359,3 +363,34 @@ def unpack_packed(packed, cu_seqlens, mask):
     _check(lib().df_unpack_packed(B, L, row_bytes, _ptr(src), _ptr(m8), _ptr(cu_seqlens.contiguous()), _ptr(out),
                                   _stream(packed.device)))
     return out
+
+
+def qkv_proj_bwd(x, w, rel, dqkv, dq_r=None, dk_r=None, num_heads: int = 1, head_dim: int = 64,
+                 workspace=None):
+    """Backward of :func:`qkv_proj` (``df_qkv_proj_bwd``). ``dqkv`` is the
+    output gradient as one ``[T, 3, H, D]`` (or ``[T, 3*H*D]``) tensor;
+    ``dq_r``, ``dk_r`` ``[H, R, D]`` when ``rel`` is given. Returns
+    ``(dx, dw, db, drel)`` (``drel`` None without ``rel``)."""
+    H, D = int(num_heads), int(head_dim)
+    T, E = x.shape
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("df_qkv_proj_bwd takes bf16 or fp16")
+    dqkv = dqkv.reshape(T, 3 * H * D).contiguous()
+    x, w = x.contiguous(), w.contiguous()
+    R = 0 if rel is None else rel.shape[0]
+    if rel is not None:
+        rel, dq_r, dk_r = rel.contiguous(), dq_r.contiguous(), dk_r.contiguous()
+    dt = DTYPE_CODES[x.dtype]
+    need = lib().df_qkv_proj_bwd_workspace_size(T, E, H, D, R, dt)
+    if need == 0:
+        raise DfError(1, "invalid projection shape")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    db = torch.empty(3 * H * D, dtype=x.dtype, device=x.device)
+    drel = torch.empty_like(rel) if rel is not None else None
+    _check(lib().df_qkv_proj_bwd(T, E, H, D, R, dt, _ptr(x), _ptr(w), _ptr(rel), _ptr(dqkv), _ptr(dq_r),
+                                 _ptr(dk_r), _ptr(dx), _ptr(dw), _ptr(db), _ptr(drel), _ptr(workspace),
+                                 workspace.numel(), _stream(x.device)))
+    return dx, dw, db, drel

@@ -593,6 +593,9 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
   p.w = w;
   p.bias = bias;
   p.K = hidden;
+  p.lda = hidden;
+  p.ldw = hidden;
+  p.kchunk = 0;
   p.HD = int(HD);
   p.D = head_dim;
   p.R = rel_rows;
@@ -666,6 +669,155 @@ int df_unpack_packed(int32_t batch, int32_t max_len, int64_t row_bytes, const vo
                                          (hipStream_t)stream),
                       "unpack")))
     return rc;
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward of the fused projections.
+
+namespace {
+
+struct ProjBwdPlan {
+  size_t wt, dyt, xt, relt, dyr, dyrt, part, total;
+  int64_t Tp, Rp;
+  int nch, kchunk;
+};
+
+ProjBwdPlan proj_bwd_plan(int64_t T, int E, int64_t HD, int R) {
+  ProjBwdPlan pl{};
+  const int64_t N3 = 3 * HD, N2 = 2 * HD;
+  pl.Tp = (T + 7) / 8 * 8;
+  pl.Rp = (int64_t(R) + 7) / 8 * 8;
+  // split the token contraction of dW into fixed chunks (a function of the
+  // shape only): about 512 work-groups
+  const int64_t tiles = ((N3 + 127) / 128) * ((int64_t(E) + 1 + 127) / 128);
+  int64_t nch = (512 + tiles - 1) / tiles;
+  int64_t kc = T > 0 ? ((T + nch - 1) / nch + 63) / 64 * 64 : 64;
+  nch = T > 0 ? (T + kc - 1) / kc : 0;
+  pl.nch = int(nch);
+  pl.kchunk = int(kc);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  pl.wt = take(size_t(E) * N3 * 2);
+  pl.dyt = take(size_t(N3) * pl.Tp * 2);
+  pl.xt = take(size_t(E + 1) * pl.Tp * 2);
+  pl.relt = take(size_t(E + 1) * pl.Rp * 2);
+  pl.dyr = take(size_t(R) * N2 * 2);
+  pl.dyrt = take(size_t(N2) * pl.Rp * 2);
+  pl.part = take(size_t(nch + 1) * N3 * (E + 1) * sizeof(float));
+  pl.total = o;
+  return pl;
+}
+
+int check_proj_dims(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim, int32_t rel_rows,
+                    int32_t dtype) {
+  if (dtype == DF_FP32)
+    return fail(DF_ERR_UNSUPPORTED, "the projections take 16-bit operands (bf16 or fp16), not fp32");
+  if (dtype != DF_BF16 && dtype != DF_FP16) return fail(DF_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(DF_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128, got %d", head_dim);
+  if (num_heads < 1 || num_heads > 65535)
+    return fail(DF_ERR_INVALID, "num_heads must be in [1, 65535], got %d", num_heads);
+  if (hidden < 8 || hidden % 8)
+    return fail(DF_ERR_INVALID, "hidden must be a positive multiple of 8, got %d", hidden);
+  if (tokens < 0 || rel_rows < 0) return fail(DF_ERR_INVALID, "tokens and rel_rows must be >= 0");
+  const int64_t HD = int64_t(num_heads) * head_dim;
+  if (tokens >= (int64_t(1) << 23) || int64_t(hidden) >= (int64_t(1) << 20) || 3 * HD >= (int64_t(1) << 20) ||
+      rel_rows >= (1 << 20))
+    return fail(DF_ERR_UNSUPPORTED, "projection too large (tokens %lld, hidden %d, heads x dim %lld)",
+                (long long)tokens, hidden, (long long)HD);
+  return DF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t df_qkv_proj_bwd_workspace_size(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim,
+                                      int32_t rel_rows, int32_t dtype) {
+  if (check_proj_dims(tokens, hidden, num_heads, head_dim, rel_rows, dtype)) return 0;
+  return proj_bwd_plan(tokens, hidden, int64_t(num_heads) * head_dim, rel_rows).total;
+}
+
+int df_qkv_proj_bwd(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim, int32_t rel_rows,
+                    int32_t dtype, const void* x, const void* w, const void* rel, const void* dqkv,
+                    const void* dq_r, const void* dk_r, void* dx, void* dw, void* db, void* drel,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_proj_dims(tokens, hidden, num_heads, head_dim, rel_rows, dtype);
+  if (rc) return rc;
+  const bool want_rel = rel != nullptr && rel_rows > 0;
+  if (!rel && rel_rows > 0) return fail(DF_ERR_INVALID, "rel is NULL but rel_rows = %d", rel_rows);
+  if ((rc = check_ptr(w, "w", 16)) || (rc = check_ptr(dw, "dw", 2)) ||
+      (tokens > 0 && ((rc = check_ptr(x, "x", 16)) || (rc = check_ptr(dqkv, "dqkv", 16)) ||
+                      (rc = check_ptr(dx, "dx", 2)))) ||
+      (want_rel && ((rc = check_ptr(rel, "rel", 16)) || (rc = check_ptr(dq_r, "dq_r", 16)) ||
+                    (rc = check_ptr(dk_r, "dk_r", 16)) || (rc = check_ptr(drel, "drel", 2)))))
+    return rc;
+  if (db && !aligned(db, 2)) return fail(DF_ERR_INVALID, "db must be 2-byte aligned");
+  const int64_t T = tokens, HD = int64_t(num_heads) * head_dim, N3 = 3 * HD, N2 = 2 * HD;
+  const int E = hidden, R = want_rel ? rel_rows : 0;
+  const ProjBwdPlan pl = proj_bwd_plan(T, E, HD, R);
+  if (workspace_bytes < pl.total)
+    return fail(DF_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", pl.total, workspace_bytes);
+  if ((rc = check_ptr(workspace, "workspace", kAlign))) return rc;
+  char* ws = (char*)workspace;
+  const hipStream_t st = (hipStream_t)stream;
+  const uint16_t one = dtype == DF_FP16 ? 0x3C00 : 0x3F80;
+  float* part = reinterpret_cast<float*>(ws + pl.part);
+
+  auto gemm = [&](const void* a, int lda, const void* b, int ldw, int M, int N, int K, int kchunk, int mode,
+                  void* out) {
+    dfa::ProjParams p{};
+    p.a = a;
+    p.w = b;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.lda = lda;
+    p.ldw = ldw;
+    p.kchunk = kchunk;
+    p.HD = N;  // mode 0: a plain [M, N] output
+    p.D = head_dim;
+    p.mode = mode;
+    p.dtype = dtype;
+    p.out0 = out;
+    return dfa::launch_proj(p, st);
+  };
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) {
+    if (e == hipSuccess) e = r;
+  };
+  // transposed operands: W^T [E][3HD]; dY^T [3HD][Tp]; x^T [E + 1][Tp] with a
+  // last row of ones (its column of the dW product is db)
+  run(dfa::launch_transpose16(w, E, 0, ws + pl.wt, N3, 0, int(N3), E, 1, st));
+  if (T > 0) {
+    run(dfa::launch_transpose16(dqkv, N3, 0, ws + pl.dyt, pl.Tp, 0, int(T), int(N3), 1, st));
+    run(dfa::launch_transpose16(x, E, 0, ws + pl.xt, pl.Tp, 0, int(T), E, 1, st));
+    run(dfa::launch_fill16(ws + pl.xt + size_t(E) * pl.Tp * 2, T, one, st));
+    // dx = dY W
+    run(gemm(dqkv, int(N3), ws + pl.wt, int(N3), int(T), E, int(N3), 0, 0, dx));
+    // dW partials over token chunks (and db in column E)
+    run(gemm(ws + pl.dyt, int(pl.Tp), ws + pl.xt, int(pl.Tp), int(N3), E + 1, int(T), pl.kchunk, 2, part));
+  }
+  if (want_rel) {
+    run(dfa::launch_transpose16(rel, E, 0, ws + pl.relt, pl.Rp, 0, R, E, 1, st));
+    run(dfa::launch_fill16(ws + pl.relt + size_t(E) * pl.Rp * 2, R, one, st));
+    run(dfa::launch_rel_rows(dq_r, dk_r, ws + pl.dyr, num_heads, R, head_dim, st));
+    run(dfa::launch_transpose16(ws + pl.dyr, N2, 0, ws + pl.dyrt, pl.Rp, 0, R, int(N2), 1, st));
+    // drel = dY_r W[:2HD]
+    run(gemm(ws + pl.dyr, int(N2), ws + pl.wt, int(N3), R, E, int(N2), 0, 0, drel));
+    // the relative rows' dW (and db) partial, after the token chunks
+    run(gemm(ws + pl.dyrt, int(pl.Rp), ws + pl.relt, int(pl.Rp), int(N2), E + 1, R, 0, 2,
+             part + size_t(pl.nch) * N3 * (E + 1)));
+  }
+  run(dfa::launch_proj_reduce(part, T > 0 ? pl.nch : 0, want_rel ? int(N2) : 0, int(N3), E, dtype, dw, db, st));
+  if ((rc = hip_check(e, "projection backward"))) return rc;
   return ok();
 }
 

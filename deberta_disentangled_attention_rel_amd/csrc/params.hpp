@@ -64,14 +64,20 @@ struct Params {
 };
 
 // One projection GEMM Y = A W^T + bias (16-bit operands, fp32 accumulation):
-// A [M, K], W rows [N, K] (both K-contiguous), bias [N] or null. mode 0:
-// column n = which * HD + hd goes to out<which>[m * HD + hd] ([T, H, D]);
-// mode 1: to out<which>[(hd / D) * R + m) * D + hd % D] ([H, R, D]).
+// A [M, K] (row stride lda), W rows [N, K] (row stride ldw), both
+// K-contiguous, bias [N] or null. mode 0: column n = which * HD + hd goes to
+// out<which>[m * HD + hd] ([T, H, D]; HD = N gives a plain [M, N]); mode 1:
+// to out<which>[(hd / D) * R + m) * D + hd % D] ([H, R, D]); mode 2: split-K
+// partials, fp32 out0[(chunk * M + m) * N + n] for the contraction range
+// [chunk * kchunk, (chunk + 1) * kchunk) of chunk = blockIdx.y (kchunk = 0:
+// all of K in one chunk).
 struct ProjParams {
   const void* a;
   const void* w;
   const void* bias;
   int M, N, K;
+  int lda, ldw;
+  int kchunk;
   int HD, D, R;
   int mode;
   int dtype;
@@ -91,7 +97,21 @@ hipError_t launch_bwd_dkv(const Params& p, hipStream_t st);
 hipError_t launch_bwd_dq(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_dw(const Params& p, hipStream_t st);
 hipError_t launch_relgrad_sum(const Params& p, hipStream_t st);
-hipError_t launch_proj(const ProjParams& p, hipStream_t st);
+hipError_t launch_proj(const ProjParams& p, hipStream_t st);  // gridDim.y = number of K chunks
+// dst[b][c][r] = src[b][r][c] for a batch of [rows, cols] 16-bit matrices
+// (row strides src_ld / dst_ld, batch strides src_bs / dst_bs); columns r in
+// [rows, dst_ld) of dst are written as zero
+hipError_t launch_transpose16(const void* src, int64_t src_ld, int64_t src_bs, void* dst, int64_t dst_ld,
+                              int64_t dst_bs, int rows, int cols, int batch, hipStream_t st);
+// fill n 16-bit elements with `bits`
+hipError_t launch_fill16(void* dst, int64_t n, uint16_t bits, hipStream_t st);
+// rows [R, 2 H D] of the relative-row gradients: row r, column
+// which * H D + h D + d = (which ? dk_r : dq_r)[h][r][d]
+hipError_t launch_rel_rows(const void* dq_r, const void* dk_r, void* dst, int H, int R, int D, hipStream_t st);
+// out[n][e] (dtype) = sum_{c < nch} part[c][n][e] + (n < nrel ? part[nch][n][e] : 0)
+// for e < E, and db[n] (dtype) likewise from column E (when db != null)
+hipError_t launch_proj_reduce(const float* part, int nch, int nrel, int M, int E, int dtype, void* out, void* db,
+                              hipStream_t st);
 hipError_t launch_pack(int B, int L, int64_t row_bytes, const void* padded, const uint8_t* mask, void* packed,
                        int32_t* cu, int32_t* max_len, hipStream_t st);
 hipError_t launch_unpack(int B, int L, int64_t row_bytes, const void* packed, const uint8_t* mask,

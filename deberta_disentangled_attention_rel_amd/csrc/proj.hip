@@ -41,7 +41,7 @@ struct ProjDma {
       voff[k] = (s < SLOTS && c < PBK / 8) ? row * ld_bytes + c * 16 : kBufSkip;
     }
   }
-  // columns k0 .. k0 + 63 of the view's rows (K = row length in elements)
+  // columns k0 .. k0 + 63 of the view's rows; columns at or past K read zero
   __device__ __forceinline__ void issue(uint16_t* lds, BufView b, int k0, int K) const {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
@@ -78,13 +78,16 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
   const int logical = xcd * qx + (xcd < rx ? xcd : rx) + slot;
   const int m0 = (logical / nn) * PBM, n0 = (logical % nn) * PBN;
 
-  const int K = p.K;
-  const T* A = (const T*)p.a + int64_t(m0) * K;
-  const T* W = (const T*)p.w + int64_t(n0) * K;
-  const BufView av = buf_view(A, uint32_t(min(PBM, p.M - m0)) * uint32_t(K) * 2u);
-  const BufView wv = buf_view(W, uint32_t(min(PBN, p.N - n0)) * uint32_t(K) * 2u);
-  ProjDma dma;
-  dma.init(K * 2);
+  // this chunk's contraction range
+  const int kb = p.kchunk > 0 ? int(blockIdx.y) * p.kchunk : 0;
+  const int K = p.kchunk > 0 ? min(p.K, kb + p.kchunk) : p.K;
+  const T* A = (const T*)p.a + int64_t(m0) * p.lda;
+  const T* W = (const T*)p.w + int64_t(n0) * p.ldw;
+  const BufView av = buf_view(A, uint32_t(min(PBM, p.M - m0)) * uint32_t(p.lda) * 2u);
+  const BufView wv = buf_view(W, uint32_t(min(PBN, p.N - n0)) * uint32_t(p.ldw) * 2u);
+  ProjDma adma, wdma;
+  adma.init(p.lda * 2);
+  wdma.init(p.ldw * 2);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -92,16 +95,16 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-  const int nk = (K + PBK - 1) / PBK;
-  dma.issue(As[0], av, 0, K);
-  dma.issue(Bs[0], wv, 0, K);
+  const int nk = K > kb ? (K - kb + PBK - 1) / PBK : 0;
+  adma.issue(As[0], av, kb, K);
+  wdma.issue(Bs[0], wv, kb, K);
   wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) {
-      dma.issue(As[buf ^ 1], av, (kt + 1) * PBK, K);
-      dma.issue(Bs[buf ^ 1], wv, (kt + 1) * PBK, K);
+      adma.issue(As[buf ^ 1], av, kb + (kt + 1) * PBK, K);
+      wdma.issue(Bs[buf ^ 1], wv, kb + (kt + 1) * PBK, K);
     }
     const T* a_s = reinterpret_cast<const T*>(As[buf]);
     const T* b_s = reinterpret_cast<const T*>(Bs[buf]);
@@ -122,6 +125,22 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
   }
 
   // lane: column n = n0 + wn*64 + 32j + li; register v: row m0 + wm*64 + 32i + acc_row(v, g)
+  if (p.mode == 2) {
+    float* part = (float*)p.out0 + int64_t(blockIdx.y) * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + 32 * j + li;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 64 + 32 * i + acc_row(v, g);
+          if (m < p.M) part[int64_t(m) * p.N + n] = acc[i][j][v];
+        }
+    }
+    return;
+  }
   const int HD = p.HD, D = p.D;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -148,10 +167,110 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
 hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const unsigned nb = unsigned((p.M + PBM - 1) / PBM) * unsigned((p.N + PBN - 1) / PBN);
+  const unsigned nch = p.kchunk > 0 ? unsigned((p.K + p.kchunk - 1) / p.kchunk) : 1u;
+  const dim3 grid(nb, nch);
   if (p.dtype == DF_FP16_T)
-    proj_kernel<DF_FP16_T><<<nb, 256, 0, st>>>(p);
+    proj_kernel<DF_FP16_T><<<grid, 256, 0, st>>>(p);
   else
-    proj_kernel<DF_BF16_T><<<nb, 256, 0, st>>>(p);
+    proj_kernel<DF_BF16_T><<<grid, 256, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Pieces of the projections' backward.
+
+namespace {
+
+// 64 x 64 tiles through LDS: coalesced reads along the source rows and
+// coalesced writes along the destination rows
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ src, int64_t src_ld,
+                                                          int64_t src_bs, uint16_t* __restrict__ dst,
+                                                          int64_t dst_ld, int64_t dst_bs, int rows, int cols) {
+  __shared__ uint16_t tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + int64_t(blockIdx.z) * src_bs;
+  uint16_t* d = dst + int64_t(blockIdx.z) * dst_bs;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < rows && c < cols) ? s[int64_t(r) * src_ld + c] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int c = c0 + k, r = r0 + tx;  // destination row c, column r
+    if (c < cols && r < dst_ld) d[int64_t(c) * dst_ld + r] = tile[tx][k];
+  }
+}
+
+__global__ void fill16_kernel(uint16_t* __restrict__ dst, int64_t n, uint16_t bits) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bits;
+}
+
+// one thread per 8 elements (16 bytes) of a destination row
+__global__ void rel_rows_kernel(const uint4* __restrict__ dq_r, const uint4* __restrict__ dk_r,
+                                uint4* __restrict__ dst, int H, int R, int D) {
+  const int cpr = D / 8;  // chunks per (head, relative row)
+  const int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_row = 2 * int64_t(H) * cpr;
+  if (n >= per_row * R) return;
+  const int64_t r = n / per_row, rest = n % per_row;
+  const int which = int(rest / (int64_t(H) * cpr)), hc = int(rest % (int64_t(H) * cpr));
+  const int h = hc / cpr, c = hc % cpr;
+  const uint4* src = which ? dk_r : dq_r;
+  dst[n] = src[(int64_t(h) * R + r) * cpr + c];
+}
+
+template <int DT>
+__global__ void proj_reduce_kernel(const float* __restrict__ part, int nch, int nrel, int M, int E,
+                                   typename Tr<DT>::T* __restrict__ out, typename Tr<DT>::T* __restrict__ db) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t N = int64_t(E) + 1;
+  if (i >= int64_t(M) * N) return;
+  const int n = int(i / N), e = int(i % N);
+  float s = 0.f;
+  for (int c = 0; c < nch; ++c) s += part[int64_t(c) * M * N + i];
+  if (n < nrel) s += part[int64_t(nch) * M * N + i];
+  if (e < E)
+    out[int64_t(n) * E + e] = Tr<DT>::from_f(s);
+  else if (db)
+    db[n] = Tr<DT>::from_f(s);
+}
+
+}  // namespace
+
+hipError_t launch_transpose16(const void* src, int64_t src_ld, int64_t src_bs, void* dst, int64_t dst_ld,
+                              int64_t dst_bs, int rows, int cols, int batch, hipStream_t st) {
+  if (cols <= 0 || batch <= 0 || dst_ld <= 0) return hipSuccess;
+  const dim3 grid(unsigned((cols + 63) / 64), unsigned((dst_ld + 63) / 64), unsigned(batch));
+  transpose16_kernel<<<grid, 256, 0, st>>>((const uint16_t*)src, src_ld, src_bs, (uint16_t*)dst, dst_ld, dst_bs,
+                                           rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill16(void* dst, int64_t n, uint16_t bits, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill16_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>((uint16_t*)dst, n, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_rel_rows(const void* dq_r, const void* dk_r, void* dst, int H, int R, int D, hipStream_t st) {
+  const int64_t n = 2 * int64_t(H) * R * (D / 8);
+  if (n <= 0) return hipSuccess;
+  rel_rows_kernel<<<unsigned((n + 255) / 256), 256, 0, st>>>((const uint4*)dq_r, (const uint4*)dk_r, (uint4*)dst,
+                                                              H, R, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_reduce(const float* part, int nch, int nrel, int M, int E, int dtype, void* out, void* db,
+                              hipStream_t st) {
+  const int64_t n = int64_t(M) * (E + 1);
+  if (n <= 0) return hipSuccess;
+  const unsigned nb = unsigned((n + 255) / 256);
+  if (dtype == DF_FP16_T)
+    proj_reduce_kernel<DF_FP16_T><<<nb, 256, 0, st>>>(part, nch, nrel, M, E, (uint16_t*)out, (uint16_t*)db);
+  else
+    proj_reduce_kernel<DF_BF16_T><<<nb, 256, 0, st>>>(part, nch, nrel, M, E, (uint16_t*)out, (uint16_t*)db);
   return hipGetLastError();
 }
 

@@ -219,6 +219,29 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
                 void* q, void* k, void* v, void* q_r, void* k_r, void* stream);
 
 
+/* Backward of df_qkv_proj (the same maps, 16-bit operands, fp32
+ * accumulation): given the output gradients dqkv [tokens, 3*H*D] (row-major:
+ * dq, dk, dv side by side per token, the layout df_attn_bwd writes with
+ * tok_stride 3*H*D and head_stride D) and, when rel is given, dq_r and dk_r
+ * [H, rel_rows, D] (as df_attn_bwd writes them), writes
+ *   dx [tokens, hidden]      = dY W
+ *   drel [rel_rows, hidden]  = dY_r W[:2HD]        (when rel is given)
+ *   dw [3*H*D, hidden]       = dY^T x + [dY_r^T rel; 0]
+ *   db [3*H*D] (or NULL)     = column sums of dY and dY_r
+ * with dY the [tokens, 3HD] gradient and dY_r the [rel_rows, 2HD] one
+ * (column h*D + d of its first half is dq_r[h][r][d], of its second half
+ * dk_r[h][r][d]). The dw sum over tokens runs in fixed chunks added in a
+ * fixed order (deterministic). The workspace is caller-owned, of at least
+ * df_qkv_proj_bwd_workspace_size() bytes, 256-byte aligned; other
+ * conventions as df_qkv_proj. */
+size_t df_qkv_proj_bwd_workspace_size(int64_t tokens, int32_t hidden, int32_t num_heads,
+                                      int32_t head_dim, int32_t rel_rows, int32_t dtype);
+int df_qkv_proj_bwd(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim,
+                    int32_t rel_rows, int32_t dtype, const void* x, const void* w, const void* rel,
+                    const void* dqkv, const void* dq_r, const void* dk_r,
+                    void* dx, void* dw, void* db, void* drel,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packing helpers for the packed layout (DisentangledFlash 1.1.1 page,
  * "Packed unpadded inference and training": right-padded [B, L, ...] input
  * becomes FlashAttention-style [total_tokens, ...] rows with cu_seqlens, and

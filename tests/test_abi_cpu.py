@@ -199,6 +199,26 @@ def test_qkv_proj_rejects_on_host(df):
     assert call(outs=(f, f, f, None, f)) == 1               # q_r missing while rel given
 
 
+def test_qkv_proj_bwd_rejects_on_host(df):
+    L = df.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert L.df_qkv_proj_bwd_workspace_size(64, 64, 2, 32, 8, 0) > 0
+    assert L.df_qkv_proj_bwd_workspace_size(64, 64, 2, 32, 8, 2) == 0    # fp32
+    assert L.df_qkv_proj_bwd_workspace_size(64, 60, 2, 32, 8, 0) == 0    # hidden % 8
+
+    def call(T=64, E=64, H=2, D=32, R=8, dt=0, ptrs=(f,) * 10, ws=1 << 40):
+        return L.df_qkv_proj_bwd(T, E, H, D, R, dt, *ptrs, f, ws, None)
+    assert call(dt=2) == 2
+    assert call(D=48) == 2
+    p = list((f,) * 10)
+    p[3] = None                                   # dqkv
+    assert call(ptrs=tuple(p)) == 1 and "dqkv" in L.df_last_error().decode()
+    p = list((f,) * 10)
+    p[2] = None                                   # rel missing while rel_rows > 0
+    assert call(ptrs=tuple(p)) == 1
+    assert call(ws=1024) == 3
+
+
 def test_pack_helpers_reject_on_host(df):
     L = df.lib()
     f = ctypes.c_void_p(FAKE)

@@ -76,3 +76,53 @@ def test_proj_metric_shape_sampled_rows():
         e = rel_l2(g, r)
         print(f"  {nm} rel-L2 {e:.2e}", flush=True)
         assert e <= 1e-2, (nm, e)
+
+
+# ----------------------------------------------------------------------------
+# backward of the projections (df_qkv_proj_bwd)
+
+def _grads(T, H, D, R, dtype, seed):
+    from synth import DTYPES
+    rng = np.random.default_rng(seed)
+    dt = DTYPES[dtype]
+    dqkv = torch.from_numpy(rng.standard_normal((T, 3, H, D))).to(dt)
+    dq_r = torch.from_numpy(rng.standard_normal((H, R, D))).to(dt)
+    dk_r = torch.from_numpy(rng.standard_normal((H, R, D))).to(dt)
+    return dqkv, dq_r, dk_r
+
+
+@pytest.mark.parametrize("T,E,H,D,R,dtype,rel", [
+    (300, 64, 2, 32, 64, "bf16", True),
+    (1000, 768, 12, 64, 512, "bf16", True),
+    (1000, 768, 12, 64, 512, "fp16", True),
+    (257, 136, 3, 32, 10, "bf16", True),
+    (129, 256, 2, 128, 0, "fp16", False),
+    (0, 64, 2, 32, 33, "bf16", True),
+    (16384, 768, 12, 64, 512, "bf16", True),
+])
+def test_proj_bwd_parity(T, E, H, D, R, dtype, rel):
+    import deberta_disentangled_attention_rel_amd as df
+    print(f"proj bwd T={T} E={E} H={H} D={D} R={R} {dtype} rel={rel}", flush=True)
+    inp = make_proj_inputs(T, E, H, D, R, dtype, seed=T + 3 * E + H, rel=rel)
+    dqkv, dq_r, dk_r = _grads(T, H, D, R, dtype, seed=T + 7)
+    f = inp.f64
+    g64 = {n: t.to(torch.float64).numpy() for n, t in (("dqkv", dqkv), ("dq_r", dq_r), ("dk_r", dk_r))}
+    ref = oracle.qkv_projection_backward(f["x"], f["w"], f.get("rel"), g64["dqkv"][:, 0], g64["dqkv"][:, 1],
+                                         g64["dqkv"][:, 2], g64["dq_r"] if rel else None,
+                                         g64["dk_r"] if rel else None, H, D)
+    x, w = inp.t["x"].cuda(), inp.t["w"].cuda()
+    rl = inp.t["rel"].cuda() if rel else None
+    args = (x, w, rl, dqkv.cuda(), dq_r.cuda() if rel else None, dk_r.cuda() if rel else None)
+    got = df.qkv_proj_bwd(*args, num_heads=H, head_dim=D)
+    again = df.qkv_proj_bwd(*args, num_heads=H, head_dim=D)
+    torch.cuda.synchronize()
+    for name, g, r, h in zip(("dx", "dw", "db", "drel"), got, ref, again):
+        if r is None:
+            assert g is None
+            continue
+        assert torch.equal(g, h), name
+        if r.size == 0:
+            continue
+        e = rel_l2(g.float().cpu().numpy(), r)
+        print(f"  {name} rel-L2 {e:.2e}", flush=True)
+        assert e <= 1e-2, (name, e)
