@@ -207,6 +207,21 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # cold-cache steps: before each, a 512 MiB fill (twice the 256 MB MALL)
+    # evicts L2 and MALL; each step is timed alone between its own events
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(min(a.steps, 10)):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    cold.sort()
+    del flush
+
     fwd_ms = timed(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws), a.steps)
     bwd_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
                                   workspace=ws, reuse_fwd_workspace=True), a.steps)
@@ -284,6 +299,8 @@ def main(argv=None) -> int:
         "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms": {"min": round(per_step[0], 4), "p10": round(pct(per_step, 0.1), 4),
                     "median": round(pct(per_step, 0.5), 4), "p90": round(pct(per_step, 0.9), 4)},
+        "step_ms_cold_cache": {"n": len(cold), "min": round(cold[0], 4), "median": round(pct(cold, 0.5), 4),
+                               "max": round(cold[-1], 4)},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "bwd_recompute_ms": round(bwd_recompute_ms, 4),
