@@ -170,3 +170,46 @@ def test_dropout_full_size_one_head():
     print({k: f"{e:.2e}" for k, (e, _) in errs.items()}, flush=True)
     bad = {k: e for k, (e, t_) in errs.items() if not (e <= t_)}
     assert not bad, bad
+
+
+def test_long_sequence_L65519_sampled_rows_and_sums():
+    """One sequence eight times the benchmark's length, ending in a ragged
+    47-row tile: O, LSE and dQ on seeded rows against the oracle's row
+    functions, sum_j dV_j = sum_i dO_i (every row of P sums to one, so this
+    holds at any size), and a bitwise-repeatable backward."""
+    import deberta_disentangled_attention_rel_amd as df
+    from synth import make_inputs
+    L, H, D, span, buckets, R = 65519, 2, 64, 512, 256, 512
+    inp = make_inputs(H, D, "bf16", span, buckets, R, seed=4242, batch=1, seqlen=L)
+    print(f"long sequence: L={L} H={H} D={D} bf16", flush=True)
+    t, km, cu = to_dev(inp)
+    out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], span, buckets, max_seqlen=L)
+    g1 = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], span, buckets, out, lse, t["dout"], max_seqlen=L)
+    g2 = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], span, buckets, out, lse, t["dout"], max_seqlen=L)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    out_h, lse_h, dq_h, dv_h = (x.float().cpu().numpy() for x in (out, lse, g1[0], g1[2]))
+    f = inp.f64
+    tol_f, tol_b = TOL["bf16"]
+    rng = np.random.default_rng(4243)
+    # the first and last rows, the ragged tail, and seeded rows in between
+    rows = np.unique(np.concatenate([[0, L - 1], L - 1 - np.arange(47),
+                                     rng.integers(0, L, size=32)]))[::2]
+    rows = np.union1d(rows, [L - 1])
+    errs = {}
+    for h in range(H):
+        o, l = oracle.forward_rows(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], span, buckets,
+                                   (0, L), h, rows)
+        d = oracle.dq_rows(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], f["dout"], span, buckets,
+                           (0, L), h, rows)
+        errs[f"out[h{h}]"] = (rel_l2(out_h[rows, h], o), tol_f)
+        errs[f"lse[h{h}]"] = (rel_l2(lse_h[h, rows], l), tol_f)
+        errs[f"dq[h{h}]"] = (rel_l2(dq_h[rows, h], d), tol_b)
+        # every dV_j is near the same vector (P is nearly uniform at this
+        # length), so their bf16 roundings (at most 2^-9 relative each) can
+        # add up coherently: the bound is 2^-9 plus the fp32 accumulation
+        errs[f"sum dv[h{h}]"] = (rel_l2(dv_h[:, h].astype(np.float64).sum(0), f["dout"][:, h].sum(0)), 4e-3)
+    print({k: f"{e:.2e}" for k, (e, _) in errs.items()}, flush=True)
+    bad = {k: e for k, (e, t_) in errs.items() if not (e <= t_)}
+    assert not bad, bad
