@@ -100,8 +100,9 @@ def recorded_traffic(stage, workload_name):
         return None
 
 
-def cpu_baseline(inp):
-    """The float64 oracle on one (sequence, head) slice of the same workload."""
+def cpu_baseline(inp, slices=3):
+    """The float64 oracle on a bounded sample of the same workload: the first
+    ``slices`` heads of the first sequence, each one (sequence, head) slice."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle
@@ -109,16 +110,19 @@ def cpu_baseline(inp):
     L = inp.lengths[0]
     f = inp.f64
     sl = slice(0, L)
-    args = [f["q"][sl, :1], f["k"][sl, :1], f["v"][sl, :1], f["q_r"][:1], f["k_r"][:1]]
+    n = min(slices, w.heads)
     t0 = time.perf_counter()
-    oracle.forward(*args, w.span, w.buckets)
-    oracle.backward(*args, f["dout"][sl, :1], w.span, w.buckets)
+    for h in range(n):
+        args = [f["q"][sl, h:h + 1], f["k"][sl, h:h + 1], f["v"][sl, h:h + 1], f["q_r"][h:h + 1],
+                f["k_r"][h:h + 1]]
+        oracle.forward(*args, w.span, w.buckets)
+        oracle.backward(*args, f["dout"][sl, h:h + 1], w.span, w.buckets)
     dt = time.perf_counter() - t0
     threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    fl = flops_fwd_bwd(1, 1, L, w.head_dim, w.rows)
+    fl = n * flops_fwd_bwd(1, 1, L, w.head_dim, w.rows)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"float64 numpy oracle, forward then backward, one (sequence, head) slice "
+            "sample": f"float64 numpy oracle, forward then backward, {n} (sequence, head) slices "
                       f"of the workload (L={L}, D={w.head_dim}, R={w.rows}); {dt:.1f} s wall; "
                       f"scaled by the same FLOP convention"}
 
