@@ -303,7 +303,8 @@ def main(argv=None) -> int:
         "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "step_ms": {"min": round(per_step[0], 4), "p10": round(pct(per_step, 0.1), 4),
                     "median": round(pct(per_step, 0.5), 4), "p90": round(pct(per_step, 0.9), 4)},
-        "step_ms_cold_cache": {"n": len(cold), "min": round(cold[0], 4), "median": round(pct(cold, 0.5), 4),
+        "step_ms_cold_cache": {"n": len(cold), "min": round(cold[0], 4), "p10": round(pct(cold, 0.1), 4),
+                               "median": round(pct(cold, 0.5), 4), "p90": round(pct(cold, 0.9), 4),
                                "max": round(cold[-1], 4)},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
