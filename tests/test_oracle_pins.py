@@ -280,6 +280,22 @@ def test_p5_zero_sums():
         assert np.abs(dC2P).max() > 0 and np.abs(dP2C).max() > 0
 
 
+def test_p5_dv_column_sum():
+    # dV = P^T dO and every row of P with a valid query sums to one (rows of
+    # masked queries are zero), so per sequence and head the dV rows add up
+    # to the dO rows of the valid queries
+    inp = _small(H=2, D=8, span=12, buckets=8, seed=11, mask_frac=0.2, lengths=[25, 14, 9])
+    dv = _run_bwd(inp)[2]
+    dout = inp.f64["dout"]
+    valid = inp.key_mask.astype(bool)
+    for b in range(inp.nseq):
+        st, en = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        want = dout[st:en][valid[st:en]].sum(axis=0)
+        np.testing.assert_allclose(dv[st:en].sum(axis=0), want, rtol=0, atol=1e-12 * (1 + np.abs(want).max()))
+    # a key-masked row receives nothing
+    assert np.abs(dv[~valid]).max() == 0.0
+
+
 # ----------------------------------------------------------------------------
 # P6: transposition identity of the literal delta(j, i) reading
 
