@@ -573,9 +573,10 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
   if (tokens < 0) return fail(DF_ERR_INVALID, "tokens must be >= 0");
   if (rel_rows < 0) return fail(DF_ERR_INVALID, "rel_rows must be >= 0");
   const int64_t HD = int64_t(num_heads) * head_dim;
-  // operand rows are addressed with 32-bit byte offsets per 128-row block
+  // operand rows are addressed with 32-bit byte offsets per 128-row block;
+  // token rows are counted in 32-bit integers
   if (int64_t(hidden) * 2 * 128 >= (int64_t(1) << 31) || 3 * HD >= (int64_t(1) << 31) ||
-      tokens * HD >= (int64_t(1) << 40))
+      tokens >= (int64_t(1) << 30) || tokens * HD >= (int64_t(1) << 40))
     return fail(DF_ERR_UNSUPPORTED, "projection too large (tokens %lld, hidden %d, heads x dim %lld)",
                 (long long)tokens, hidden, (long long)HD);
   int rc;
@@ -728,6 +729,8 @@ int check_proj_dims(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t h
     return fail(DF_ERR_INVALID, "hidden must be a positive multiple of 8, got %d", hidden);
   if (tokens < 0 || rel_rows < 0) return fail(DF_ERR_INVALID, "tokens and rel_rows must be >= 0");
   const int64_t HD = int64_t(num_heads) * head_dim;
+  // the transposed operands' rows (tokens long) are addressed with 32-bit
+  // byte offsets per 128-row block
   if (tokens >= (int64_t(1) << 23) || int64_t(hidden) >= (int64_t(1) << 20) || 3 * HD >= (int64_t(1) << 20) ||
       rel_rows >= (1 << 20))
     return fail(DF_ERR_UNSUPPORTED, "projection too large (tokens %lld, hidden %d, heads x dim %lld)",

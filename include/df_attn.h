@@ -213,7 +213,9 @@ int df_attn_bwd_dropout(const df_attn_shape* shape,
  * DF_ERR_UNSUPPORTED); head_dim in {32, 64, 128}; hidden a positive multiple
  * of 8; x, w and rel 16-byte aligned. All pointers are caller-owned device
  * pointers; nothing is allocated; work is enqueued on `stream`; errors as
- * for df_attn_fwd (checked on the host before anything is enqueued). */
+ * for df_attn_fwd (checked on the host before anything is enqueued).
+ * DF_ERR_UNSUPPORTED also for tokens >= 2^30, hidden >= 2^23 or
+ * tokens * H * D >= 2^40. */
 int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim, int32_t rel_rows,
                 int32_t dtype, const void* x, const void* w, const void* bias, const void* rel,
                 void* q, void* k, void* v, void* q_r, void* k_r, void* stream);
@@ -233,7 +235,9 @@ int df_qkv_proj(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_
  * dk_r[h][r][d]). The dw sum over tokens runs in fixed chunks added in a
  * fixed order (deterministic). The workspace is caller-owned, of at least
  * df_qkv_proj_bwd_workspace_size() bytes, 256-byte aligned; other
- * conventions as df_qkv_proj. */
+ * conventions as df_qkv_proj. DF_ERR_UNSUPPORTED for tokens >= 2^23,
+ * hidden >= 2^20, 3*H*D >= 2^20 or rel_rows >= 2^20 (the workspace size is
+ * then 0). */
 size_t df_qkv_proj_bwd_workspace_size(int64_t tokens, int32_t hidden, int32_t num_heads,
                                       int32_t head_dim, int32_t rel_rows, int32_t dtype);
 int df_qkv_proj_bwd(int64_t tokens, int32_t hidden, int32_t num_heads, int32_t head_dim,

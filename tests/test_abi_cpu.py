@@ -197,6 +197,8 @@ def test_qkv_proj_rejects_on_host(df):
     assert call(outs=(f, None, f, f, f)) == 1               # k missing
     assert call(rel=None) == 1                               # rel_rows > 0 without rel
     assert call(outs=(f, f, f, None, f)) == 1               # q_r missing while rel given
+    assert call(T=1 << 30, H=1) == 2                         # token rows counted in 32 bits
+    assert call(E=1 << 23) == 2                              # 128-row blocks of x past 2 GiB
 
 
 def test_qkv_proj_bwd_rejects_on_host(df):
@@ -217,6 +219,8 @@ def test_qkv_proj_bwd_rejects_on_host(df):
     p[2] = None                                   # rel missing while rel_rows > 0
     assert call(ptrs=tuple(p)) == 1
     assert call(ws=1024) == 3
+    assert call(T=1 << 23) == 2                              # transposed rows of 2^23 tokens
+    assert L.df_qkv_proj_bwd_workspace_size(1 << 23, 64, 2, 32, 8, 0) == 0
 
 
 def test_pack_helpers_reject_on_host(df):
