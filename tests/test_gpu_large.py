@@ -213,3 +213,25 @@ def test_long_sequence_L65519_sampled_rows_and_sums():
     print({k: f"{e:.2e}" for k, (e, _) in errs.items()}, flush=True)
     bad = {k: e for k, (e, t_) in errs.items() if not (e <= t_)}
     assert not bad, bad
+
+
+def test_workload3_bwd_reusing_forward_workspace():
+    """The benchmark's launch configuration at full size: the backward runs on
+    the forward's workspace (index tables and strips kept) and must equal,
+    bit for bit, the recomputing backward that the workload-3 test compares
+    with the oracle on the same seeded inputs."""
+    import deberta_disentangled_attention_rel_amd as df
+    inp = workload_inputs(3)
+    w = inp.workload
+    print(f"workload 3 ({w.name}): backward reusing the forward's workspace", flush=True)
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    args = (t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets)
+    shape = df.make_shape(t["q"].view(-1, *t["q"].shape[-2:]), inp.nseq, inp.max_seqlen)
+    ws = torch.empty(df.workspace_size(1, shape, w.span, w.buckets), dtype=torch.uint8, device="cuda")
+    out, lse = df.fwd(*args, workspace=ws, **kw)
+    g_reuse = df.bwd(*args, out, lse, t["dout"], workspace=ws, reuse_fwd_workspace=True, **kw)
+    g_fresh = df.bwd(*args, out, lse, t["dout"], **kw)
+    torch.cuda.synchronize()
+    for n_, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g_reuse, g_fresh):
+        assert torch.equal(a, b), n_
