@@ -235,3 +235,11 @@ def test_workload3_bwd_reusing_forward_workspace():
     torch.cuda.synchronize()
     for n_, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g_reuse, g_fresh):
         assert torch.equal(a, b), n_
+    # the timed dropout step (p = 0.1) the same way
+    dk = dict(kw, dropout_p=0.1, seed=1234, offset=0)
+    out, lse = df.fwd(*args, workspace=ws, **dk)
+    g_reuse = df.bwd(*args, out, lse, t["dout"], workspace=ws, reuse_fwd_workspace=True, **dk)
+    g_fresh = df.bwd(*args, out, lse, t["dout"], **dk)
+    torch.cuda.synchronize()
+    for n_, a, b in zip(("dq", "dk", "dv", "dq_r", "dk_r"), g_reuse, g_fresh):
+        assert torch.equal(a, b), "dropout " + n_
