@@ -18,6 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["lib", "Shape", "build_rel_index", "workspace_size", "supported", "fwd", "fwd_inference", "bwd",
+           "rel_rows",
            "qkv_proj", "qkv_proj_bwd", "pack_padded", "unpack_packed",
            "profile_enable", "profile_read", "DfError", "DTYPE_CODES", "LIB_PATH"]
 
@@ -166,6 +167,53 @@ def _layout(q, k, v, cu_seqlens, max_seqlen):
     return q3, k3, v3, batch, L
 
 
+def rel_rows(span: int, buckets: int) -> int:
+    """R = 2 * att, att = buckets if buckets > 0 else span: the row count that
+    q_r, k_r, dq_r and dk_r must have."""
+    return 2 * (int(buckets) if int(buckets) > 0 else int(span))
+
+
+def _check_args(q3, k3, v3, q_r, k_r, span, buckets, key_mask, cu_seqlens):
+    """Reject, before any library call, tensors whose raw pointers the
+    kernels would read with a shape, dtype or device other than the one the
+    shape block describes (the C ABI cannot see tensor metadata)."""
+    if q3.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q3.dtype}")
+    for name, t in (("k", k3), ("v", v3)):
+        if t.shape != q3.shape or t.dtype != q3.dtype or t.device != q3.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device "
+                             f"({tuple(t.shape)} {t.dtype} {t.device} vs {tuple(q3.shape)} {q3.dtype} {q3.device})")
+    T, H, D = q3.shape
+    R = rel_rows(span, buckets)
+    for name, t in (("q_r", q_r), ("k_r", k_r)):
+        if t.shape != (H, R, D) or t.dtype != q3.dtype or t.device != q3.device:
+            raise ValueError(f"{name} must be [H, R, D] = {(H, R, D)} (R = 2*att for span {span}, buckets {buckets})"
+                             f" in q's dtype and device, got {tuple(t.shape)} {t.dtype} {t.device}")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q3.device:
+            raise ValueError(f"cu_seqlens must be a 1-D int32 tensor on {q3.device}, got "
+                             f"{cu_seqlens.dtype} {tuple(cu_seqlens.shape)} {cu_seqlens.device}")
+        if not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be contiguous with batch + 1 >= 2 entries")
+    if key_mask is not None:
+        if key_mask.dtype not in (torch.uint8, torch.bool) or key_mask.device != q3.device:
+            raise ValueError(f"key_mask must be uint8 or bool on {q3.device}, got {key_mask.dtype} {key_mask.device}")
+        if key_mask.numel() != T or not key_mask.is_contiguous():
+            raise ValueError(f"key_mask must be contiguous with T = {T} elements, got {key_mask.numel()}")
+
+
+def _require_gpu(q3):
+    if q3.device.type != "cuda":
+        raise ValueError(f"q, k, v must be on a GPU device, got {q3.device}")
+
+
+def _check_lse(lse, q3):
+    T, H, _ = q3.shape
+    if lse.dtype != torch.float32 or lse.shape != (H, T) or not lse.is_contiguous() or lse.device != q3.device:
+        raise ValueError(f"lse must be a contiguous float32 [H, T] = {(H, T)} tensor on {q3.device}, got "
+                         f"{lse.dtype} {tuple(lse.shape)} {lse.device}")
+
+
 def profile_enable(on: bool) -> None:
     """Turn per-launch HIP event timing inside the library on or off."""
     _check(lib().df_attn_profile_enable(1 if on else 0))
@@ -216,15 +264,18 @@ def fwd(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_seqlens=No
     ``(seed, offset)``; pass the same values to ``bwd``). ``p2c`` is the P2C
     row convention: "literal" (delta(j, i)) or "shared" (the C2P row)."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    _require_gpu(q3)
+    _check_args(q3, k3, v3, q_r, k_r, span, buckets, key_mask, cu_seqlens)
     shape = make_shape(q3, batch, L, p2c)
     T, H, D = q3.shape
     if out is None:
         out = torch.empty_like(q3)
     out3 = _as_thd(out)
-    if out3.shape != q3.shape or not out3.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q")
+    if out3.shape != q3.shape or not out3.is_contiguous() or out3.dtype != q3.dtype or out3.device != q3.device:
+        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype and device")
     if lse is None:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check_lse(lse, q3)
     ws = _workspace(0, shape, span, buckets, q.device, workspace)
     q_r, k_r = q_r.contiguous(), k_r.contiguous()
     if dropout_p:
@@ -243,12 +294,14 @@ def fwd_inference(q, k, v, q_r, k_r, span: int, buckets: int, key_mask=None, cu_
                   max_seqlen: Optional[int] = None, out=None, workspace=None, p2c: str = "literal"):
     """Inference forward (no LSE, nothing kept for a backward). Returns ``out``."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    _require_gpu(q3)
+    _check_args(q3, k3, v3, q_r, k_r, span, buckets, key_mask, cu_seqlens)
     shape = make_shape(q3, batch, L, p2c)
     if out is None:
         out = torch.empty_like(q3)
     out3 = _as_thd(out)
-    if out3.shape != q3.shape or not out3.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped like q")
+    if out3.shape != q3.shape or not out3.is_contiguous() or out3.dtype != q3.dtype or out3.device != q3.device:
+        raise ValueError("out must be a contiguous tensor shaped like q, in q's dtype and device")
     ws = _workspace(0, shape, span, buckets, q.device, workspace)
     q_r, k_r = q_r.contiguous(), k_r.contiguous()
     _check(lib().df_attn_fwd_inference(ctypes.byref(shape), _ptr(q3), _ptr(k3), _ptr(v3), _ptr(q_r),
@@ -268,17 +321,26 @@ def bwd(q, k, v, q_r, k_r, span: int, buckets: int, out, lse, dout, key_mask=Non
     (sized for the backward) and still holds its index tables and strips
     (DF_FLAG_BWD_REUSE_FWD)."""
     q3, k3, v3, batch, L = _layout(q, k, v, cu_seqlens, max_seqlen)
+    _require_gpu(q3)
+    _check_args(q3, k3, v3, q_r, k_r, span, buckets, key_mask, cu_seqlens)
+    _check_lse(lse, q3)
     if reuse_fwd_workspace and workspace is None:
         raise ValueError("reuse_fwd_workspace needs the forward's workspace")
     shape = make_shape(q3, batch, L, p2c, FLAG_BWD_REUSE_FWD if reuse_fwd_workspace else 0)
     out3, dout3 = _as_thd(out).contiguous(), _as_thd(dout).contiguous()
+    for name, t in (("out", out3), ("dout", dout3)):
+        if t.shape != q3.shape or t.dtype != q3.dtype or t.device != q3.device:
+            raise ValueError(f"{name} must be shaped like q, in q's dtype and device")
     if grads is None:
         grads = (torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3),
                  torch.empty_like(q_r), torch.empty_like(k_r))
     dq, dk, dv, dq_r, dk_r = grads
     for g_ in (dq, dk, dv):
-        if _as_thd(g_).shape != q3.shape or not g_.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous tensors shaped like q")
+        if _as_thd(g_).shape != q3.shape or not g_.is_contiguous() or g_.dtype != q3.dtype or g_.device != q3.device:
+            raise ValueError("dq, dk, dv must be contiguous tensors shaped like q, in q's dtype and device")
+    for g_ in (dq_r, dk_r):
+        if g_.shape != q_r.shape or not g_.is_contiguous() or g_.dtype != q3.dtype or g_.device != q3.device:
+            raise ValueError("dq_r, dk_r must be contiguous tensors shaped like q_r ([H, R, D]), in q's dtype")
     ws = _workspace(1, shape, span, buckets, q.device, workspace)
     q_r, k_r = q_r.contiguous(), k_r.contiguous()
     if dropout_p:

@@ -25,7 +25,7 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wno-unused-result",
+    "-Wno-unused-result",
     # per-thread arrays stay in registers (never silently moved to LDS, which
     # would change a kernel's LDS budget and occupancy)
     "-mllvm", "-disable-promote-alloca-to-lds",

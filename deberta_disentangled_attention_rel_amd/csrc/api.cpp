@@ -369,6 +369,11 @@ struct Dropout {
 int set_dropout(dfa::Params& prm, const Dropout* d) {
   if (!d || d->p == 0.f) return DF_OK;
   if (!(d->p > 0.f && d->p < 1.f)) return fail(DF_ERR_INVALID, "dropout probability must be in [0, 1), got %g", double(d->p));
+  // the backward carries dS = P (dP / (1 - p) - Delta) as a 16-bit MFMA
+  // operand; in fp16 (largest value 65504) keep 1 / (1 - p) <= 1000
+  if (prm.dtype == dfa::DF_FP16_T && d->p > 0.999f)
+    return fail(DF_ERR_UNSUPPORTED, "fp16 dropout needs dropout_p <= 0.999 (1/(1-p) must stay small in fp16), got %g",
+                double(d->p));
   prm.drop = 1;
   const double thr = std::floor(double(d->p) * 4294967296.0);
   prm.drop_thr = thr >= 4294967295.0 ? 0xffffffffu : uint32_t(thr);

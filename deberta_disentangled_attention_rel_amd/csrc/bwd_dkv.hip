@@ -303,10 +303,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         const int il = half_major_partner<NQT>(u, g, v);
         P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]) + bj);
         if constexpr (DROP) {
-          // dV takes P F, dS = P (F dP - Delta), F = keep / (1 - p)
-          const float F = wd[v] >= p.drop_thr ? p.drop_scale : 0.f;
-          dS[v] = P[v] * (dP[v] * F - dlt_s[buf][il]);
-          P[v] *= F;
+          // dS = P (F dP - Delta), F = keep / (1 - p); dV takes P keep (the
+          // 1 / (1 - p) factor multiplies dV once at the end)
+          const bool keep = wd[v] >= p.drop_thr;
+          dS[v] = P[v] * (dP[v] * (keep ? p.drop_scale : 0.f) - dlt_s[buf][il]);
+          P[v] = keep ? P[v] : 0.f;
         } else {
           dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
         }
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int c = 32 * nd + acc_row(v, g);
-      dvp[c] = TR::from_f(dVt[nd][v]);
+      dvp[c] = TR::from_f(DROP ? dVt[nd][v] * p.drop_scale : dVt[nd][v]);
       dkp[c] = TR::from_f(dKt[nd][v] * p.scale);
     }
 }

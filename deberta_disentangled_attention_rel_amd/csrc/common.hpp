@@ -200,9 +200,9 @@ __device__ __forceinline__ uint4 buf_load16(BufView b, int voff, int soff = 0) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention-probability dropout (DisentangledFlash 1.1.1 page, "Status": the
-// dropout runs inside the fused kernels and its Philox mask is regenerated in
-// the backward). Philox4x32 with 10 rounds, written from its definition
+// Attention-probability dropout (DisentangledFlash 1.1.1 page, "Status":
+// dropout is applied inside the fused kernels and the backward recomputes the
+// mask from the Philox counter). Philox4x32 with 10 rounds, written from its definition
 // (Salmon, Moraes, Dror and Shaw, SC 2011): a round maps counter
 // (c0, c1, c2, c3) and key (k0, k1) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
 // hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key grows by (W0, W1) before every

@@ -304,9 +304,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
           ls = TR::sum(pf[t][q], ls);
         }
       if constexpr (DROP) {
-        // the row sum above is of the undropped P; P V takes the dropped and
-        // rescaled P. Registers 4k..4k+3 of a subtile hold four consecutive
-        // keys, one Philox call.
+        // the row sum above is of the undropped P; P V takes the dropped P
+        // (kept or zero, unscaled: the 1 / (1 - p) factor multiplies O once
+        // at the end, so the 16-bit operand never holds P / (1 - p)).
+        // Registers 4k..4k+3 of a subtile hold four consecutive keys, one
+        // Philox call.
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
             const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h), p.drop_off,
                                             p.seed_lo, p.seed_hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[t][4 * k4 + e] = r.w[e] >= p.drop_thr ? y[t][4 * k4 + e] * p.drop_scale : 0.f;
+            for (int e = 0; e < 4; ++e) y[t][4 * k4 + e] = r.w[e] >= p.drop_thr ? y[t][4 * k4 + e] : 0.f;
           }
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   const float lt = l + xor32(l);
   if (!qin) return;
   const bool ok = qvalid && lt > 0.f;
-  const float inv = ok ? 1.f / lt : 0.f;
+  const float inv = ok ? (DROP ? p.drop_scale : 1.f) / lt : 0.f;
   T* op = (T*)p.out + tok_i * p.ts + int64_t(h) * p.hs;
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd)

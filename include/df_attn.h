@@ -62,7 +62,7 @@ typedef enum { DF_BF16 = 0, DF_FP16 = 1, DF_FP32 = 2 } df_dtype;
 
 enum {
   DF_OK = 0,
-  DF_ERR_INVALID = 1,      /* null pointer, bad shape/stride/alignment, R mismatch */
+  DF_ERR_INVALID = 1,      /* null pointer, bad shape/stride/alignment/index parameters */
   DF_ERR_UNSUPPORTED = 2,  /* head_dim not in {32,64,128}, unknown dtype */
   DF_ERR_WORKSPACE = 3,    /* workspace smaller than df_attn_workspace_size() */
   DF_ERR_HIP = 4           /* a HIP launch reported an error */
@@ -102,7 +102,10 @@ enum { DF_FLAG_BWD_REUSE_FWD = 1 };
  * df_attn_fwd/df_attn_bwd accept this shape and index configuration, else the
  * error code they would return. `span` is DeBERTa's max_relative_positions
  * (>= 1), `buckets` its position_buckets (0 = no log bucketing; otherwise
- * >= 2, with span-1 > buckets/2). Host only; touches no device. */
+ * >= 2, with span-1 > buckets/2). The shape is checked against the packed
+ * contract (cu_seqlens given): the padded layout (cu_seqlens NULL) further
+ * needs total_tokens == batch*max_seqlen, which df_attn_fwd/df_attn_bwd
+ * check and this function does not. Host only; touches no device. */
 int df_attn_supported(const df_attn_shape* shape, int32_t span, int32_t buckets);
 
 /* Bytes of workspace needed by df_attn_fwd (pass 0) or df_attn_bwd (pass 1);
@@ -124,7 +127,10 @@ int df_build_rel_index(int32_t max_seqlen, int32_t span, int32_t buckets,
                        int32_t* c2p_lut, int32_t* p2c_lut, void* stream);
 
 /* Forward pass: writes out [T,H,D] (dtype) and lse [H,T] (fp32, natural log;
- * -inf on masked rows). q_r and k_r must have R = 2*att rows. */
+ * -inf on masked rows). q_r and k_r must have R = 2*att rows: the library
+ * sees only their pointers and cannot check this, so the caller (or the
+ * Python binding, which does) must ensure it; fewer rows make the kernels
+ * read past the allocation. */
 int df_attn_fwd(const df_attn_shape* shape,
                 const void* q, const void* k, const void* v,
                 const void* q_r, const void* k_r,
@@ -163,9 +169,9 @@ int df_attn_bwd(const df_attn_shape* shape,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Training forward and backward with attention-probability dropout
- * (DisentangledFlash 1.1.1 page, "Status": the dropout runs inside the fused
- * kernels and its Philox mask is regenerated in the backward instead of being
- * stored). After the softmax each probability is kept with probability
+ * (DisentangledFlash 1.1.1 page, "Status": dropout is applied inside the
+ * fused kernels; the backward recomputes the mask from the Philox counter
+ * rather than reading a saved one). After the softmax each probability is kept with probability
  * 1 - dropout_p and scaled by 1 / (1 - dropout_p), or set to 0; the LSE is
  * that of the undropped scores. The mask is a function of (seed, offset) and
  * the pair: for sequence n, head h, local query i and local key j, word j % 4
@@ -173,7 +179,9 @@ int df_attn_bwd(const df_attn_shape* shape,
  * (seed mod 2^32, seed >> 32) keeps the pair iff it is >= floor(p * 2^32).
  * The backward must be called with the forward's (dropout_p, seed, offset).
  * Arguments otherwise as df_attn_fwd / df_attn_bwd; dropout_p must be in
- * [0, 1) (DF_ERR_INVALID otherwise); dropout_p = 0 is the plain path. */
+ * [0, 1) (DF_ERR_INVALID otherwise; for DF_FP16 at most 0.999, else
+ * DF_ERR_UNSUPPORTED, since the backward carries dP / (1 - dropout_p) in fp16
+ * operands); dropout_p = 0 is the plain path. */
 int df_attn_fwd_dropout(const df_attn_shape* shape,
                         const void* q, const void* k, const void* v,
                         const void* q_r, const void* k_r,

@@ -10,9 +10,9 @@ with M0 = 0xD2511F53, M1 = 0xCD9E8D57 (32 x 32 -> 64-bit products); the key is
 bumped by the Weyl constants W0 = 0x9E3779B9, W1 = 0xBB67AE85 before every
 round after the first; 10 rounds.
 
-Attention dropout (DisentangledFlash 1.1.1 page, "Status": attention-
-probability dropout runs inside the fused kernels and its Philox mask is
-regenerated in the backward pass instead of being stored). The pages do not
+Attention dropout (DisentangledFlash 1.1.1 page, "Status": the fused kernels
+apply dropout to the attention probabilities, and the backward recomputes the
+mask from the Philox counter rather than saving it). The pages do not
 fix the counter layout; the reading used here (and by the kernels):
 for sequence n of the batch, head h, local query i and local key j,
     counter = (j // 4, i, n * H + h, offset),  key = (seed mod 2^32, seed >> 32)

@@ -162,6 +162,12 @@ def test_dropout_entry_points_reject_on_host(df):
     rc = L.df_attn_fwd_dropout(ctypes.byref(s), *vp[:5], 512, 256, None, None, 0.1, 1, 0, vp[5], None,
                                ctypes.c_void_p(FAKE), 1 << 40, None)
     assert rc == 1
+    # fp16 keeps 1 / (1 - p) <= 1000: the backward carries dP / (1 - p) in fp16 operands
+    s16 = _shape(df, dtype=1)
+    for fn, args in ((L.df_attn_fwd_dropout, [*vp[:5], 512, 256, None, None, 0.9995, 1, 0, vp[5], vp[6]]),
+                     (L.df_attn_bwd_dropout, [*p15[:5], 512, 256, None, None, 0.9995, 1, 0, *p15[5:13]])):
+        rc = fn(ctypes.byref(s16), *args, ctypes.c_void_p(FAKE), 1 << 40, None)
+        assert rc == 2 and "fp16" in L.df_last_error().decode()
 
 
 def test_bwd_and_index_reject_on_host(df):
@@ -279,3 +285,73 @@ def test_narrow_criterion(span, buckets):
         assert steps <= 1
     if buckets == 256 and span in (260, 200, 131):
         assert not narrow and steps > 1   # these really skip rows
+
+
+# ---------------------------------------------------------------------------
+# Binding-side checks: the C ABI sees only raw pointers, so the binding
+# rejects tensors whose shape, dtype or device differ from what the shape
+# block tells the kernels, before any library call.
+
+def _cpu_args(T=64, H=2, D=32, span=32, buckets=0, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    R = 2 * (buckets if buckets > 0 else span)
+    q = torch.zeros(T, H, D, dtype=dtype)
+    qr = torch.zeros(H, R, D, dtype=dtype)
+    return dict(q3=q, k3=q.clone(), v3=q.clone(), q_r=qr, k_r=qr.clone(), span=span, buckets=buckets,
+                key_mask=None, cu_seqlens=None)
+
+
+def test_binding_accepts_consistent_args(df):
+    import torch
+    a = _cpu_args()
+    df._check_args(**a)
+    a["key_mask"] = torch.ones(64, dtype=torch.uint8)
+    a["cu_seqlens"] = torch.tensor([0, 30, 64], dtype=torch.int32)
+    df._check_args(**a)
+    a["key_mask"] = torch.ones(64, dtype=torch.bool)
+    df._check_args(**a)
+
+
+@pytest.mark.parametrize("case", [
+    "qr_rows_span", "kr_rows", "qr_dtype", "k_shape", "v_dtype", "cu_int64", "cu_2d", "mask_len",
+    "mask_dtype", "bucket_rows"])
+def test_binding_rejects_inconsistent_args(df, case):
+    import torch
+    a = _cpu_args()
+    if case == "qr_rows_span":      # span rows instead of 2*att
+        a["q_r"] = torch.zeros(2, 32, 32, dtype=torch.bfloat16)
+    elif case == "kr_rows":
+        a["k_r"] = torch.zeros(2, 66, 32, dtype=torch.bfloat16)
+    elif case == "qr_dtype":
+        a["q_r"] = a["q_r"].to(torch.float16)
+    elif case == "k_shape":
+        a["k3"] = torch.zeros(64, 2, 64, dtype=torch.bfloat16)
+    elif case == "v_dtype":
+        a["v3"] = a["v3"].float()
+    elif case == "cu_int64":        # torch's default integer type
+        a["cu_seqlens"] = torch.tensor([0, 30, 64])
+    elif case == "cu_2d":
+        a["cu_seqlens"] = torch.tensor([[0, 30, 64]], dtype=torch.int32)
+    elif case == "mask_len":
+        a["key_mask"] = torch.ones(63, dtype=torch.uint8)
+    elif case == "mask_dtype":
+        a["key_mask"] = torch.ones(64, dtype=torch.int32)
+    elif case == "bucket_rows":     # buckets 16 need R = 32 rows, q_r has 64
+        a["buckets"] = 16
+    with pytest.raises(ValueError):
+        df._check_args(**a)
+
+
+def test_binding_rejects_host_tensors_and_bad_lse(df):
+    import torch
+    a = _cpu_args()
+    with pytest.raises(ValueError, match="GPU"):
+        df.fwd(a["q3"], a["k3"], a["v3"], a["q_r"], a["k_r"], 32, 0, max_seqlen=64)
+    with pytest.raises(ValueError, match="GPU"):
+        df.bwd(a["q3"], a["k3"], a["v3"], a["q_r"], a["k_r"], 32, 0, a["q3"], torch.zeros(2, 64),
+               a["q3"], max_seqlen=64)
+    df._check_lse(torch.zeros(2, 64), a["q3"])
+    for bad in (torch.zeros(64, 2), torch.zeros(2, 64, dtype=torch.float64), torch.zeros(2, 128)[:, ::2]):
+        with pytest.raises(ValueError):
+            df._check_lse(bad, a["q3"])

@@ -63,7 +63,16 @@ def test_packed_attention_through_helpers():
     q_r, k_r = (torch.from_numpy(rng.standard_normal((H, R, D)) / 8).to(torch.bfloat16).cuda() for _ in range(2))
     md = torch.from_numpy(m).cuda()
     (qp, cu, mx), (kp, _, _), (vp, _, _) = (df.pack_padded(t, md) for t in (q, k, v))
-    out_p, _ = df.fwd(qp, kp, vp, q_r, k_r, span, buckets, cu_seqlens=cu, max_seqlen=mx)
+    out_p, lse_p = df.fwd(qp, kp, vp, q_r, k_r, span, buckets, cu_seqlens=cu, max_seqlen=mx)
+    # the same packed forward on inputs packed by the oracle's helper
+    packed_ref = [oracle.pack_padded(t.cpu().view(torch.int16).numpy(), m) for t in (q, k, v)]
+    ref_cu, ref_mx = packed_ref[0][1], packed_ref[0][2]
+    qo, ko, vo = (torch.from_numpy(pr[0]).view(torch.bfloat16).cuda() for pr in packed_ref)
+    out_o, lse_o = df.fwd(qo, ko, vo, q_r, k_r, span, buckets, cu_seqlens=torch.from_numpy(ref_cu).cuda(),
+                          max_seqlen=ref_mx)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out_o.view(torch.int16))
+    assert torch.equal(lse_p, lse_o)
     out_u = df.unpack_packed(out_p, cu, md).float().cpu().numpy()
     out_pad, _ = df.fwd(q, k, v, q_r, k_r, span, buckets, key_mask=md.reshape(-1))
     ref = (out_pad.float().cpu().numpy() * m[:, :, None, None])

@@ -1,6 +1,6 @@
 """Pins for the oracle's attention dropout (DisentangledFlash 1.1.1 page,
-"Status": attention-probability dropout inside the fused kernels, its Philox
-mask regenerated in the backward).
+"Status": dropout of the attention probabilities inside the fused kernels,
+the mask recomputed from its counter in the backward).
 
 * Philox4x32-10 against two known-answer vectors of the generator's reference
   implementation (Salmon et al., SC 2011; counter / key all zero, and the
