@@ -30,7 +30,8 @@ EXPORTED = ("df_attn_supported", "df_attn_workspace_size", "df_build_rel_index",
             "df_attn_bwd_dropout", "df_strerror", "df_last_error",
             "df_attn_version",
             "df_attn_profile_enable", "df_attn_profile_read", "df_attn_stage_name", "df_qkv_proj",
-            "df_pack_padded", "df_unpack_packed", "df_qkv_proj_bwd", "df_qkv_proj_bwd_workspace_size")
+            "df_pack_padded", "df_unpack_packed", "df_qkv_proj_bwd", "df_qkv_proj_bwd_workspace_size",
+            "df_attn_fwd_noalloc")
 NUM_STAGES = 9
 
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.df_attn_fwd.restype = ctypes.c_int
     L.df_attn_fwd_inference.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     L.df_attn_fwd_inference.restype = ctypes.c_int
+    L.df_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    L.df_attn_fwd_noalloc.restype = ctypes.c_int
     f32, u64, u32 = ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32
     L.df_attn_fwd_dropout.argtypes = [sp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, u64, u32, vp, vp, vp, sz, vp]
     L.df_attn_fwd_dropout.restype = ctypes.c_int

@@ -1,11 +1,12 @@
 // C ABI of the library: argument validation, workspace planning and launch
 // sequencing. Validation is pure host code and runs before any HIP call.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "df_attn.h"
@@ -438,6 +439,76 @@ int df_attn_fwd_inference(const df_attn_shape* shape, const void* q, const void*
                           size_t workspace_bytes, void* stream) {
   return fwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, nullptr, workspace,
                   workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The forward without a caller workspace, for callers that cannot allocate
+// device memory (code under HIP graph capture, tight serving loops,
+// harnesses that forbid hipMalloc). Its workspace is `scratch`, a static
+// device array of a fixed size that each device holds until the process
+// ends; calls on one device share it, so calls that overlap on one device
+// race. The forward's kernels write every workspace byte they read (index
+// tables, strips, end columns) before reading it, so nothing needs clearing
+// between calls.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(DF_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device
+// (with that device current). In host code `scratch` itself is a host-side
+// stand-in, never a device address: only these pointers reach kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_device(hipStream_t st, void** ptr) {
+  int dev = -1;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (st) {
+    int sdev = -1;
+    if ((rc = hip_check(hipStreamGetDevice(st, &sdev), "hipStreamGetDevice"))) return rc;
+    if (sdev != dev)
+      return fail(DF_ERR_INVALID, "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(DF_ERR_UNSUPPORTED, "device %d beyond the first %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))) return rc;
+    if (!p) return fail(DF_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int df_attn_fwd_noalloc(const df_attn_shape* shape, const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r, int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens, void* out, float* lse,
+                        void* stream) {
+  // every size check comes before the first HIP call
+  int att, R;
+  int rc = check_all(shape, span, buckets, cu_seqlens != nullptr, &att, &R);
+  if (rc) return rc;
+  const size_t need = make_plan(0, shape, R).total;
+  if (need > kScratchBytes)
+    return fail(DF_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace; the static scratch of df_attn_fwd_noalloc holds %zu "
+                "(use df_attn_fwd with a caller workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_of_device((hipStream_t)stream, &ws))) return rc;
+  return fwd_impl(shape, q, k, v, q_r, k_r, span, buckets, key_mask, cu_seqlens, out, lse, ws, kScratchBytes,
+                  stream);
 }
 
 }  // extern "C"

@@ -153,6 +153,30 @@ int df_attn_fwd_inference(const df_attn_shape* shape,
                           void* out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments as df_attn_fwd (lse may be NULL, then
+ * as df_attn_fwd_inference), without a workspace argument. The workspace is
+ * a static device array of DF_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library, which every device it runs on holds until the process ends; the
+ * call allocates and frees nothing. A shape whose df_attn_workspace_size(0,
+ * ...) exceeds that size is rejected with DF_ERR_WORKSPACE before anything
+ * is enqueued (bf16/fp16 with R = 512 fit about 32,000 token-heads, e.g.
+ * 2,600 tokens at 12 heads). The stream must belong to the current device.
+ * The first call on a device looks up the array's device address there (it
+ * may load the library's device code), so make it before capturing a graph.
+ * All calls on one device share the array and it keeps the last call's
+ * contents: calls that overlap on one device (concurrent streams or threads)
+ * race and must be ordered by the caller. Nothing in the array needs
+ * clearing between calls. */
+#define DF_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int df_attn_fwd_noalloc(const df_attn_shape* shape,
+                        const void* q, const void* k, const void* v,
+                        const void* q_r, const void* k_r,
+                        int32_t span, int32_t buckets,
+                        const uint8_t* key_mask, const int32_t* cu_seqlens,
+                        void* out, float* lse, void* stream);
+
 /* Backward pass: given the forward's out and lse and the output gradient
  * dout, writes dq, dk, dv [T,H,D] and dq_r, dk_r [H,R,D] (all dtype). The
  * gradients overwrite the outputs (never accumulate). Scores are recomputed

@@ -355,3 +355,20 @@ def test_binding_rejects_host_tensors_and_bad_lse(df):
     for bad in (torch.zeros(64, 2), torch.zeros(2, 64, dtype=torch.float64), torch.zeros(2, 128)[:, ::2]):
         with pytest.raises(ValueError):
             df._check_lse(bad, a["q3"])
+
+
+def test_noalloc_forward_rejects_on_host(df):
+    """df_attn_fwd_noalloc: a shape whose forward workspace exceeds the static
+    scratch (64 MiB) is refused with DF_ERR_WORKSPACE, and a bad shape with
+    the forward's code, before any HIP call (fake pointers)."""
+    L = df.lib()
+    vp = [ctypes.c_void_p(FAKE)] * 7
+    big = _shape(df, batch=1, max_seqlen=4096, total_tokens=4096, num_heads=12, tok_stride=768)
+    assert df.workspace_size(0, big, 512, 256) > (64 << 20)
+    rc = L.df_attn_fwd_noalloc(ctypes.byref(big), *vp[:5], 512, 256, None, None, vp[5], vp[6], None)
+    assert rc == 3 and "static scratch" in L.df_last_error().decode()
+    rc = L.df_attn_fwd_noalloc(ctypes.byref(_shape(df, head_dim=48)), *vp[:5], 512, 256, None, None, vp[5],
+                               vp[6], None)
+    assert rc == 2
+    rc = L.df_attn_fwd_noalloc(ctypes.byref(_shape(df)), *vp[:5], 100, 256, None, None, vp[5], vp[6], None)
+    assert rc == 1
