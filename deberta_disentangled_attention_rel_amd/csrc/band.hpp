@@ -116,7 +116,7 @@ struct WinDma {
   // Copy strip rows row0 + r (clamped to nvalid - 1), columns from
   // start_of(k, r) (a multiple of 8, k = this thread's instruction index).
   template <class StartFn>
-  static __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid,
+  static __device__ __forceinline__ void issue(T* lds, const T* strip, int RP, int row0, int nvalid,
                                                StartFn start_of) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
@@ -164,7 +164,7 @@ struct C2PWindowDma {
       start[k] = p.c2p[n];  // raw: rounded when the copy is issued, so nothing waits for it here
     }
   }
-  __device__ __forceinline__ void issue(T* lds, const T* __restrict__ strip, int RP, int row0, int nvalid) const {
+  __device__ __forceinline__ void issue(T* lds, const T* strip, int RP, int row0, int nvalid) const {
     W::issue(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k] & ~7; });
   }
 };

@@ -140,6 +140,21 @@ __device__ __forceinline__ constexpr int acc_row(int v, int g) { return 8 * (v >
 template <int E>
 __device__ __forceinline__ constexpr int fed_row(int q, int s, int g) { return acc_row(q * E + s, g); }
 
+// An accumulator tile whose register v holds src[acc_row(v, g)]: a value per
+// row of the tile (four 16-byte LDS reads), to start an MFMA chain from.
+__device__ __forceinline__ f32x16 bias16(const float* src, int g) {
+  f32x16 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 b = *reinterpret_cast<const float4*>(src + 8 * k + 4 * g);
+    r[4 * k] = b.x;
+    r[4 * k + 1] = b.y;
+    r[4 * k + 2] = b.z;
+    r[4 * k + 3] = b.w;
+  }
+  return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -266,6 +281,48 @@ __device__ __forceinline__ void quad_transpose(uint32_t& w0, uint32_t& w1, uint3
       w1 = x;
       w3 = y;
     }
+  }
+}
+
+// Two gathered raw values (C2P term, P2C term) of a pair held until they are
+// added: for 16-bit types one 32-bit register (the halves are loaded
+// separately, so each load completes on its own), for fp32 two.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <typename T> struct RawPair {
+  using type = u16x2;
+  static __device__ __forceinline__ void set(type& r, T c, T p) {
+    r.x = c;
+    r.y = p;
+  }
+  template <typename TR>
+  static __device__ __forceinline__ float add2(type r, float c) {
+    return TR::add2(r.x, r.y, c);
+  }
+};
+template <> struct RawPair<float> {
+  struct type {
+    float c, p;
+  };
+  static __device__ __forceinline__ void set(type& r, float c, float p) {
+    r.c = c;
+    r.p = p;
+  }
+  template <typename TR>
+  static __device__ __forceinline__ float add2(type r, float c) {
+    return (r.c + r.p) + c;
+  }
+};
+
+// An empty asm statement that reads x: the value is then computed before
+// this point (it cannot sink past it into a later block).
+template <typename F>
+__device__ __forceinline__ void keep_here(const F& x) {
+  if constexpr (sizeof(F) == 16) {
+    const uint4 u = __builtin_bit_cast(uint4, x);
+    asm volatile("" ::"v"(u.x), "v"(u.y), "v"(u.z), "v"(u.w));
+  } else {
+    static_assert(sizeof(F) == 4, "one or four registers");
+    asm volatile("" ::"v"(x));
   }
 }
 

@@ -226,7 +226,7 @@ struct DmaTile {
   static constexpr int SLOTS = ROWS * PC;
   static constexpr int NI = (SLOTS + NT - 1) / NT;
 
-  static __device__ __forceinline__ void issue(T* lds, const T* __restrict__ base, int64_t ts, int row0, int nvalid) {
+  static __device__ __forceinline__ void issue(T* lds, const T* base, int64_t ts, int row0, int nvalid) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
