@@ -115,9 +115,16 @@ struct WinDma {
   }
   // Copy strip rows row0 + r (clamped to nvalid - 1), columns from
   // start_of(k, r) (a multiple of 8, k = this thread's instruction index).
+  // The strip is read through a buffer view of the sequence's strip rows
+  // (RP elements each): buffer LDS-DMA copies, unlike global ones, let the
+  // compiler see that later LDS reads of other buffers do not depend on
+  // them.
+  // Copy strip rows row0 + r (clamped to nvalid - 1), columns from
+  // start_of(k, r), with global LDS-DMA loads from `strip` (the strip rows
+  // of the sequence and head).
   template <class StartFn>
-  static __device__ __forceinline__ void issue(T* lds, const T* strip, int RP, int row0, int nvalid,
-                                               StartFn start_of) {
+  static __device__ __forceinline__ void issue_global(T* lds, const T* strip, int RP, int row0, int nvalid,
+                                                      StartFn start_of) {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
@@ -133,6 +140,31 @@ struct WinDma {
         const int col = min(start_of(k, rr) + chunk * 8, RP - 8);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(strip + int64_t(r) * RP + col),
                                          (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16, 0, 0);
+      }
+    }
+  }
+  template <class StartFn>
+  static __device__ __forceinline__ void issue(T* lds, BufView strip, int RP, int row0, int nvalid,
+                                               StartFn start_of) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int s0 = k * NT + wave * 64;
+      if (s0 >= SLOTS) break;  // wave-uniform
+      const int s = k * NT + int(threadIdx.x);
+      if (s < SLOTS) {
+        int row, chunk;
+        slot(s, row, chunk);
+        const int rr = row < 0 ? 0 : row;
+        const int r = min(row0 + rr, nvalid - 1);
+        // chunks past the strip row are never read; keep the copy in bounds
+        const int col = min(start_of(k, rr) + chunk * 8, RP - 8);
+        // device pass only: in the host pass this builtin inside the kernels'
+        // lambdas silently drops the kernels' launch stubs
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(strip.r, (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16,
+                                                 (r * RP + col) * int(sizeof(T)), 0, 0, 0);
+#endif
       }
     }
   }
@@ -165,7 +197,7 @@ struct C2PWindowDma {
     }
   }
   __device__ __forceinline__ void issue(T* lds, const T* strip, int RP, int row0, int nvalid) const {
-    W::issue(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k] & ~7; });
+    W::issue_global(lds, strip, RP, row0, nvalid, [&](int k, int) { return start[k] & ~7; });
   }
 };
 

@@ -47,7 +47,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
 
   __shared__ __align__(16) T Qs[2][BM * QP];
   __shared__ __align__(16) T dOs[2][BM * QP];
-  __shared__ __align__(16) float uq_s[2][BM];   // per-query (C2P end) - LSE*log2e, -inf if masked
+  // per query: ((C2P end) - LSE*log2e) / (s*log2e) (-inf if masked), the
+  // start of its score accumulator; and -Delta, the start of its dP
+  // accumulator
+  __shared__ __align__(16) float uq_s[2][BM];
   __shared__ __align__(16) float dlt_s[2][BM];
   __shared__ uint32_t lut_s[2][NL];
   // strip windows of band tiles: 16-bit types copy the next band tile's
@@ -89,6 +92,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   }
   const T* ends = (const T*)p.ends + int64_t(h) * T_;
   const float kbias = kvalid ? 0.f : -INFINITY;
+  const float inv_sl = 1.f / p.scale_log2;
   const float b_end0 = TR::to_f(ends[2 * HT + tok_j]) + kbias;  // P2C column 0
   const float b_end1 = TR::to_f(ends[3 * HT + tok_j]) + kbias;  // P2C column R-1
   const T* c2pstrip = (const T*)p.c2ps + (int64_t(h) * T_ + sq.start) * RP;
@@ -158,8 +162,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if (tid < BM) {
       const bool ok = i0 + tid < sq.len && m_raw != 0u;
       const float a = cls != TILE_BAND ? TR::to_f(a_raw) : 0.f;
-      uq_s[buf][tid] = ok ? a - lse_raw * kLog2e : -INFINITY;
-      dlt_s[buf][tid] = ok ? dlt_raw : 0.f;
+      uq_s[buf][tid] = ok ? (a - lse_raw * kLog2e) * inv_sl : -INFINITY;
+      dlt_s[buf][tid] = ok ? -dlt_raw : 0.f;
     }
     // both 16-bit halves scale to byte offsets at once (narrow: (R-1)*ES fits 16 bits)
     if (tid < NL) lut_s[buf][tid] = NARROW ? lreg * ES : lreg;
@@ -184,12 +188,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if (jin && g == 0) walk_open<TR>(wrow, R, rc);
   }
 
+  // the sequence's strip rows of this head, for the window copies
+  const BufView c2pview = buf_view(c2pstrip, uint32_t(sq.len) * uint32_t(RP * ES));
+  const BufView p2cview = buf_view(p2cstrip, uint32_t(sq.len) * uint32_t(RP * ES));
   // windows of the band tile whose table slice is in lut_s[lb]
   [[maybe_unused]] auto issue_windows = [&](int lb, int i0n) {
     if constexpr (AWIN) {
-      WcW::issue(reinterpret_cast<uint16_t*>(Wc), reinterpret_cast<const uint16_t*>(c2pstrip), RP, i0n, sq.len,
+      WcW::issue(reinterpret_cast<uint16_t*>(Wc), c2pview, RP, i0n, sq.len,
                  [&](int, int r) { return win_start_bytes<ES>(lut_c(lut_s[lb][r])) / ES; });
-      WpW::issue(reinterpret_cast<uint16_t*>(Wp), reinterpret_cast<const uint16_t*>(p2cstrip), RP, j0, sq.len,
+      WpW::issue(reinterpret_cast<uint16_t*>(Wp), p2cview, RP, j0, sq.len,
                  [&](int, int r) { return win_start_bytes<ES>(lut_p(lut_s[lb][NL - 1 - r])) / ES; });
       if (tid < BM) cb_s[tid] = WcW::row_offset(tid) * ES - win_start_bytes<ES>(lut_c(lut_s[lb][tid]));
     }
@@ -212,6 +219,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     const int buf = qb & 1;
     const int i0 = qb * BM;
     const int cls = cls_of(qb);
+    [[maybe_unused]] const bool next_band = qb + 1 < nqb && cls_of(qb + 1) == TILE_BAND;
     if (qb + 1 < nqb) prefetch(qb + 1);
     if constexpr (NARROW && !AWIN) {
       if (cls == TILE_BAND) {
@@ -239,9 +247,9 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     float colsum = 0.f;
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
-      // per-query terms of this subtile: the far C2P value minus the LSE, plus
-      // in band tiles the gathered C2P + P2C terms (one block per subtile, so
-      // the 16 gathers are in flight together)
+      // band tiles: the gathered C2P + P2C terms of this subtile's pairs (one
+      // block per subtile, so the 16 gathers are in flight together); the
+      // per-query C2P value minus the LSE seeds the score accumulator
       float rel[16];
       if (cls == TILE_BAND) {
 #pragma unroll
@@ -250,28 +258,29 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           const uint32_t e = lut_s[buf][il - jl + BN - 1];
           if constexpr (NARROW) {
             rel[v] = TR::add2(*reinterpret_cast<const T*>(reinterpret_cast<const char*>(Wc) + cb_s[il] + lut_c(e)),
-                              *reinterpret_cast<const T*>(wp + lut_p(e)), uq_s[buf][il]);
+                              *reinterpret_cast<const T*>(wp + lut_p(e)), kbias);
           } else {
             const int ii = min(i0 + il, sq.len - 1);
             rel[v] = TR::add2(c2pstrip[int64_t(ii) * RP + lut_c(e)],
-                              p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)], uq_s[buf][il]);
+                              p2cstrip[int64_t(jin ? jw : sq.len - 1) * RP + lut_p(e)], kbias);
           }
         }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) rel[v] = uq_s[buf][half_major_partner<NQT>(u, g, v)];
       }
       if constexpr (AWIN) {
-        if (u == NQT - 1 && qb + 1 < nqb && cls_of(qb + 1) == TILE_BAND) {
+        if (u == NQT - 1 && next_band) {
           // this tile's last gather is issued: publish the next tile's table
-          // slice, wait for every wave to be done with the windows, then copy
-          // the next tile's windows while this tile finishes
+          // slice and wait for every wave to be done with the windows; the
+          // next tile's windows are copied once this tile's MFMAs have read
+          // their operands (an LDS-DMA copy in flight makes the compiler
+          // hold back the transposing reads that follow it)
           if (tid < NL) lut_s[buf ^ 1][tid] = NARROW ? lreg * ES : lreg;
           __syncthreads();
-          issue_windows(buf ^ 1, i0 + BM);
         }
       }
-      f32x16 S = zero16(), dP = zero16();
+      // registers v of this lane group hold the subtile's queries ib + v
+      const int ib = half_major_partner<NQT>(u, g, 0);
+      f32x16 S = seq16(&uq_s[buf][ib]);
+      f32x16 dP = DROP ? zero16() : seq16(&dlt_s[buf][ib]);  // dP - Delta without dropout
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         S = TR::mma(ld_row<TR>(Qs[buf], QP, 32 * u + li, q * KS + g * E), Kf[q], S);
@@ -298,24 +307,31 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           wd[4 * c + 3] = w3;
         }
       }
+      if (cls == TILE_BAND) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]));
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) P[v] = fast_exp2(fmaf(S[v], p.scale_log2, bj));
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int il = half_major_partner<NQT>(u, g, v);
-        P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]) + bj);
         if constexpr (DROP) {
           // dS = P (F dP - Delta), F = keep / (1 - p); dV takes P keep (the
           // 1 / (1 - p) factor multiplies dV once at the end)
           const bool keep = wd[v] >= p.drop_thr;
-          dS[v] = P[v] * (dP[v] * (keep ? p.drop_scale : 0.f) - dlt_s[buf][il]);
+          dS[v] = P[v] * fmaf(dP[v], keep ? p.drop_scale : 0.f, dlt_s[buf][ib + v]);
           P[v] = keep ? P[v] : 0.f;
         } else {
-          dS[v] = P[v] * (dP[v] - dlt_s[buf][il]);
+          dS[v] = P[v] * dP[v];
         }
       }
+      float cs = 0.f;  // far tiles: this lane's part of the column sum (of the rounded dS the MFMA uses)
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q) {
         const frag pb = TR::pack(&P[q * E]);
         const frag sb = TR::pack(&dS[q * E]);
+        cs = TR::sum(sb, cs);
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
           dVt[nd] = TR::mma(ld_col<TR>(dOs[buf], QP, 32 * u, 32 * nd, q), pb, dVt[nd]);
@@ -324,10 +340,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       }
       if (cls != TILE_BAND) {
         // far tiles: one row, one sum per tile
-        float cs = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cs += dS[v];
-        colsum += cs + xor32(cs);
+        colsum += cs;
       } else {
         // dP2C: this half's queries of the subtile, in order (their rows
         // are read in one batch, so the walk waits on LDS once)
@@ -343,7 +356,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
             walk_step<TR, false>(wrow, R, wk, wr[v], dS[v], jin && i0 + half_major_partner<NQT>(u, g, v) < sq.len);
       }
     }
+    if constexpr (AWIN) {
+      if (next_band) issue_windows(buf ^ 1, i0 + BM);
+    }
     if (cls != TILE_BAND) {
+      colsum += xor32(colsum);  // the key's two lane halves
       if (jin && g == 0) {
         walk_step<TR, NARROW>(wrow, R, wk, cls == TILE_FAR_LEFT ? 0 : R - 1, colsum);
         rc = wk.r;

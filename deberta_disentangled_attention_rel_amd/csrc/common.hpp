@@ -155,6 +155,30 @@ __device__ __forceinline__ f32x16 bias16(const float* src, int g) {
   return r;
 }
 
+// An accumulator tile whose register v holds src[v] (four 16-byte LDS
+// reads), for partners laid out half-major (register v of a lane group is
+// partner base + v).
+__device__ __forceinline__ f32x16 seq16(const float* src) {
+  f32x16 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 b = *reinterpret_cast<const float4*>(src + 4 * k);
+    r[4 * k] = b.x;
+    r[4 * k + 1] = b.y;
+    r[4 * k + 2] = b.z;
+    r[4 * k + 3] = b.w;
+  }
+  return r;
+}
+
+// An accumulator tile with every register equal to x.
+__device__ __forceinline__ f32x16 splat16(float x) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x;
+  return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
