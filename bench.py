@@ -43,6 +43,10 @@ def flops_fwd_bwd(B, H, L, D, R):
     return B * H * (14.0 * L * L * D + 16.0 * L * R * D)
 
 
+# MI355X dense fp32 MFMA peak (the strict-fp32 path's matrix products)
+PEAK_FP32_TFLOPS = 157.3
+
+
 def kernel_algorithmic_flops(stage, B, H, L, D, R):
     """Algorithmic FLOPs of one launch of a stage (matrix products it must run)."""
     per = B * H * L * L * D
@@ -121,10 +125,86 @@ def cpu_baseline(inp, slices=3):
     threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     fl = n * flops_fwd_bwd(1, 1, L, w.head_dim, w.rows)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "slices_timed": n, "slices_in_workload": inp.nseq * w.heads,
+            "seconds_per_slice": round(dt / n, 3),
             "sample": f"float64 numpy oracle, forward then backward, {n} (sequence, head) slices "
                       f"of the workload (L={L}, D={w.head_dim}, R={w.rows}); {dt:.1f} s wall; "
                       f"scaled by the same FLOP convention"}
+
+
+def dist(xs):
+    """min / p10 / median / p90 of a list of per-call milliseconds."""
+    xs = sorted(xs)
+
+    def pct(q):
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+    return {"n": len(xs), "min": round(xs[0], 4), "p10": round(pct(0.1), 4), "median": round(pct(0.5), 4),
+            "p90": round(pct(0.9), 4)}
+
+
+def per_call(fn, n):
+    """Milliseconds of each of n calls, each between its own events."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+
+def other_workload(df, n, dtype, backward, reps):
+    """Throughput of the other workloads (parity cases of the same path): the
+    L=512 bf16 forward, the packed varlen D=128 forward+backward and the
+    L=8192 D=128 unbucketed stress forward+backward in fp16 and strict fp32.
+    FLOPs by the same convention, per sequence with its own active row count;
+    percent of the MFMA peak of the working dtype (bf16/fp16: 2516.6, fp32:
+    157.3 TFLOP/s)."""
+    import torch
+    from synth import workload_inputs
+    dev = torch.device("cuda", 0)
+    inp = workload_inputs(n, dtype=dtype)
+    w = inp.workload
+    H, D = w.heads, w.head_dim
+    t = {k_: v_.to(dev) for k_, v_ in inp.t.items()}
+    km = None if inp.key_mask is None else torch.from_numpy(inp.key_mask).to(dev)
+    cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
+    shape = df.make_shape(t["q"], inp.nseq, inp.max_seqlen)
+    ws = torch.empty(max(df.workspace_size(0, shape, w.span, w.buckets),
+                         df.workspace_size(1, shape, w.span, w.buckets)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((H, t["q"].shape[0]), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(t[x]) for x in ("q", "k", "v", "q_r", "k_r"))
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen, workspace=ws)
+
+    def step():
+        df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out=out, lse=lse, **kw)
+        if backward:
+            df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out, lse, t["dout"],
+                   grads=grads, reuse_fwd_workspace=True, **kw)
+    step()
+    times = per_call(step, reps)
+    fl = 0.0
+    c2p, _ = df.build_rel_index(inp.max_seqlen, w.span, w.buckets, device=dev)
+    for Lk in inp.lengths:
+        # active rows at length Lk: distinct table values over |d| < Lk
+        mid = inp.max_seqlen - 1
+        r_k = int(torch.unique(c2p[mid - (Lk - 1): mid + Lk]).numel()) if Lk > 0 else 0
+        per = 4.0 * Lk * Lk * D + 4.0 * Lk * r_k * D
+        if backward:
+            per += 10.0 * Lk * Lk * D + 12.0 * Lk * r_k * D
+        fl += H * per
+    d = dist(times)
+    peak = PEAK_FP32_TFLOPS if (dtype or w.dtype) == "fp32" else PEAK_BF16_TFLOPS
+    tf = fl / (d["median"] * 1e-3) / 1e12
+    del ws, t, grads
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "dtype": dtype or w.dtype, "passes": "fwd+bwd" if backward else "fwd",
+            "tokens": int(inp.total_tokens), "sequences": int(inp.nseq), "heads": H, "head_dim": D,
+            "rel_rows": w.rows, "ms": d, "tflops": round(tf, 2), "peak_tflops": round(peak, 1),
+            "pct_peak": round(100.0 * tf / peak, 2)}
 
 
 def main(argv=None) -> int:
@@ -134,6 +214,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads' timings (for profiler runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times), "
                          "the reference for scaling memory counters to bytes")
@@ -226,9 +308,13 @@ def main(argv=None) -> int:
     cold.sort()
     del flush
 
-    fwd_ms = timed(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws), a.steps)
-    bwd_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
-                                  workspace=ws, reuse_fwd_workspace=True), a.steps)
+    # the two passes alone, each call between its own events
+    fwd_calls = per_call(lambda: df.fwd(q, k, v, q_r, k_r, w.span, w.buckets, out=out, lse=lse, workspace=ws),
+                         a.steps)
+    bwd_calls = per_call(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout, grads=grads,
+                                        workspace=ws, reuse_fwd_workspace=True), a.steps)
+    fwd_ms = sum(fwd_calls) / len(fwd_calls)
+    bwd_ms = sum(bwd_calls) / len(bwd_calls)
     # the backward on its own, recomputing the index tables and strips
     bwd_recompute_ms = timed(lambda: df.bwd(q, k, v, q_r, k_r, w.span, w.buckets, out, lse, dout,
                                             grads=grads, workspace=ws), a.steps)
@@ -265,6 +351,15 @@ def main(argv=None) -> int:
     proj_bwd_ms = timed(lambda: df.qkv_proj_bwd(pt["x"], pt["w"], pt["rel"], pg, pr, pr, H, D, workspace=pws),
                         a.steps)
     del pt, pouts, pg, pr, pws
+
+    # the other workloads, unless skipped (profiler runs)
+    others = []
+    if not a.headline_only:
+        del ws, grads, out, out_inf, lse_d
+        torch.cuda.empty_cache()
+        for n_, dt_, bw_, reps in ((2, None, False, 20), (4, None, True, 10), (5, "fp16", True, 5),
+                                   (5, "fp32", True, 3)):
+            others.append(other_workload(df, n_, dt_, bw_, reps))
 
     ms = (t1 - t0) * 1e3 / a.steps
     fl = flops_fwd_bwd(B, H, L, D, r_active)
@@ -308,6 +403,8 @@ def main(argv=None) -> int:
                                "max": round(cold[-1], 4)},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "fwd_ms_dist": dist(fwd_calls),
+        "bwd_ms_dist": dist(bwd_calls),
         "bwd_recompute_ms": round(bwd_recompute_ms, 4),
         "bwd_reuses_fwd_strips": True,
         "inference_fwd_ms": round(inf_ms, 4),
@@ -321,6 +418,7 @@ def main(argv=None) -> int:
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dom, w.name)},
         "kernels": kern,
+        "other_workloads": others,
         "device": torch.cuda.get_device_properties(dev).name,
         "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
     }

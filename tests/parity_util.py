@@ -70,3 +70,27 @@ def compare(inp, gpu, ref, backward=True):
     bad = {n: e for n, e in errs.items()
            if not np.isfinite(e) or e > (tol_f if n in ("out", "lse") else tol_b)}
     return errs, bad
+
+
+# Per-row gate at the full sizes: a tensor-wide rel-L2 over 16,384 rows can
+# hide a few wrong rows (one zeroed row adds only ~0.8%), so every compared
+# row is also checked on its own. A row's error is its L2 error over its
+# reference norm, the norm floored at ROW_FLOOR times the RMS row norm (a
+# masked row, whose reference is exactly zero, must then come out near zero).
+# The bound is ROW_MULT times the tensor tolerance: a zeroed or sign-flipped
+# row scores 1 or 2, far above it, while bf16 rounding of a 32..128-element
+# row stays well below it.
+ROW_MULT = 4.0
+ROW_FLOOR = 0.05
+
+
+def max_row_err(x, ref) -> float:
+    """Largest per-row relative L2 error of x against ref (rows = axis 0)."""
+    x = np.asarray(x, dtype=np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(len(ref), -1)
+    if ref.size == 0:
+        return 0.0
+    rn = np.linalg.norm(ref, axis=1)
+    rms = float(np.sqrt(np.mean(rn ** 2)))
+    den = np.maximum(rn, ROW_FLOOR * rms) if rms > 0 else np.ones_like(rn)
+    return float(np.max(np.linalg.norm(x - ref, axis=1) / den))

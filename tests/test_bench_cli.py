@@ -28,3 +28,9 @@ def test_flop_convention():
     assert bench.kernel_algorithmic_flops("bwd_dkv", B, H, L, D, R) == 8 * per + 2 * rel
     assert bench.kernel_algorithmic_flops("bwd_dq", B, H, L, D, R) == 6 * per + 2 * rel
     assert bench.kernel_algorithmic_flops("delta", B, H, L, D, R) is None
+
+
+def test_latency_distribution_fields():
+    import bench
+    d = bench.dist([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert d == {"n": 5, "min": 1.0, "p10": 1.0, "median": 3.0, "p90": 5.0}

@@ -6,7 +6,9 @@ The oracle cannot evaluate every head of the large workloads in seconds, so
 output tensor, including dq_r / dk_r, which sum over all sequences) and the
 other heads on 64 seeded query rows (O, LSE and dQ need only their own row).
 Tolerances (rel-L2 per tensor): bf16/fp16 forward 1e-2, gradients 2e-2;
-fp32 1e-5. The long unbucketed stress workload also checks that two backward
+fp32 1e-5; every compared row also on its own, within ROW_MULT times the
+tensor tolerance (parity_util.max_row_err), so that a few wrong rows cannot
+hide in a tensor-wide figure. The long unbucketed stress workload also checks that two backward
 runs are bitwise identical.
 """
 import numpy as np
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 from synth import workload_inputs, WORKLOADS
-from parity_util import rel_l2, TOL, to_dev
+from parity_util import rel_l2, TOL, to_dev, max_row_err, ROW_MULT
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -53,7 +55,12 @@ def _check(n, dtype=None, backward=True, p2c="literal"):
         valid = np.isfinite(lse[h])
         assert np.array_equal(np.isfinite(gpu["lse"][h]), valid)
         errs[f"out[h{h}]"] = (rel_l2(gpu["out"][:, h], out[:, h]), tol_f)
+        errs[f"out rows[h{h}]"] = (max_row_err(gpu["out"][:, h], out[:, h]), ROW_MULT * tol_f)
         errs[f"lse[h{h}]"] = (rel_l2(gpu["lse"][h][valid], lse[h][valid]), tol_f)
+        # each valid row's LSE to the same relative bound
+        errs[f"lse rows[h{h}]"] = (float(np.max(np.abs(gpu["lse"][h][valid] - lse[h][valid]) /
+                                                np.maximum(np.abs(lse[h][valid]), 1.0))) if valid.any() else 0.0,
+                                   ROW_MULT * tol_f)
     if backward:
         g = oracle.backward(f["q"], f["k"], f["v"], f["q_r"], f["k_r"], f["dout"], w.span,
                             w.buckets, heads=full, **kw)
@@ -62,6 +69,7 @@ def _check(n, dtype=None, backward=True, p2c="literal"):
                 a = gpu[name][:, h] if name in ("dq", "dk", "dv") else gpu[name][h]
                 b = ref[:, h] if name in ("dq", "dk", "dv") else ref[h]
                 errs[f"{name}[h{h}]"] = (rel_l2(a, b), tol_b)
+                errs[f"{name} rows[h{h}]"] = (max_row_err(a, b), ROW_MULT * tol_b)
     # other heads: sampled query rows
     seqs = oracle.sequences(inp.total_tokens, inp.cu_seqlens, inp.nseq)
     rest = [h for h in range(H) if h not in full]
@@ -86,9 +94,11 @@ def _check(n, dtype=None, backward=True, p2c="literal"):
         assert np.array_equal(np.isfinite(gl_), np.isfinite(rl_))
         v = np.isfinite(rl_)
         errs["out[sampled rows]"] = (rel_l2(np.concatenate(go), np.concatenate(ro)), tol_f)
+        errs["out[each sampled row]"] = (max_row_err(np.concatenate(go), np.concatenate(ro)), ROW_MULT * tol_f)
         errs["lse[sampled rows]"] = (rel_l2(gl_[v], rl_[v]), tol_f)
         if backward:
             errs["dq[sampled rows]"] = (rel_l2(np.concatenate(gq), np.concatenate(rq)), tol_b)
+            errs["dq[each sampled row]"] = (max_row_err(np.concatenate(gq), np.concatenate(rq)), ROW_MULT * tol_b)
     print({k: f"{e:.2e}" for k, (e, _) in errs.items()}, flush=True)
     bad = {k: e for k, (e, t) in errs.items() if not (e <= t)}
     assert not bad, bad

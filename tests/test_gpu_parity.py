@@ -63,6 +63,13 @@ CASES = {
                                     buckets=16, seed=10, mask_frac=0.25),
     "bf16_big_bucket_odd": dict(L=400, H=2, D=64, span=300, buckets=256, seed=11),
     "bf16_metric_index_L1024": dict(L=1024, H=1, D=64, span=512, buckets=256, seed=12),
+    # tables that skip rows (mid - 1 > mid ln((span-1)/mid)): the general
+    # kernel instantiations, which gather both relative terms from global
+    # memory and walk with skipped rows, in other dtypes and head dims
+    "fp32_D128_wide_bucket": dict(L=260, H=1, D=128, dtype="fp32", span=100, buckets=128, seed=13),
+    "fp16_D32_wide_bucket": dict(L=180, H=2, D=32, dtype="fp16", span=100, buckets=128, seed=14),
+    "bf16_D128_wide_bucket_masked": dict(lengths=[170, 41, 96], H=2, D=128, span=100, buckets=128, seed=15,
+                                         mask_frac=0.2),
 }
 
 
@@ -172,6 +179,8 @@ DROP_CASES = {
     "bf16_packed_masked": (0.2, 77, 9),
     "fp16_D128_unbucketed": (0.15, 3, 1),
     "tiny_fp32_L64": (0.5, 1, 2),
+    "bf16_big_bucket_odd": (0.25, 99, 4),      # tables that skip rows
+    "fp32_D128_wide_bucket": (0.1, 5, 0),
 }
 
 
