@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   // masked query: P = 0 through an infinite LSE
   const float lse2 = qvalid ? p.lse[int64_t(h) * T_ + tok_i] * kLog2e : INFINITY;
   const float dlt = qvalid ? p.delta[int64_t(h) * T_ + tok_i] : 0.f;
+  const float inv_sl = 1.f / p.scale_log2;
   const T* ends = (const T*)p.ends + int64_t(h) * T_;
   const float a_end0 = TR::to_f(ends[tok_i]);
   const float a_end1 = TR::to_f(ends[HT + tok_i]);
@@ -128,9 +129,11 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
     const int cls = cls_of(kb);
     kt.template store<KP>(Ks[buf]);
     vt.template store<KP>(Vs[buf]);
+    // per key: far tiles its P2C end value divided by s log2 e (it seeds the
+    // score accumulator), band tiles 0; -inf if masked
     if (tid < BN) {
       const bool ok = j0 + tid < sq.len && m_raw != 0u;
-      bj_s[buf][tid] = ok ? (cls != TILE_BAND ? TR::to_f(e_raw) : 0.f) : -INFINITY;
+      bj_s[buf][tid] = ok ? (cls != TILE_BAND ? TR::to_f(e_raw) * inv_sl : 0.f) : -INFINITY;
     }
     // both 16-bit halves scale to byte offsets at once (narrow: (R-1)*ES fits 16 bits)
     if (tid < NL) lut_s[buf][tid] = NARROW ? lreg * ES : lreg;
@@ -152,14 +155,21 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
   }
 
   const int nkb = (sq.len + BN - 1) / BN;
+  // the key tiles fall into three contiguous ranges: far-left (tile kb with
+  // i0 - kb*BN - BN + 1 >= d_hi), band, far-right (i0 + BM - 1 - kb*BN <=
+  // d_lo); each range runs its own loop, so the far loops carry none of the
+  // band tiles' gathers, windows and walk state
+  const int nl = i0 - BN + 1 - d_hi;
+  const int kb_band = min(nkb, nl >= 0 ? nl / BN + 1 : 0);
+  const int kb_right = max(kb_band, min(nkb, (i0 + BM - 1 - d_lo + BN - 1) / BN));
   prefetch(0);
   commit(0);
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto iter = [&](int kb, auto band_c) __attribute__((always_inline)) {
     const int buf = kb & 1;
     const int j0 = kb * BN;
-    const int cls = cls_of(kb);
+    const int cls = decltype(band_c)::value ? TILE_BAND : cls_of(kb);
     if (kb + 1 < nkb) prefetch(kb + 1);
 
     // the tile body, compiled once per tile class as straight-line code
@@ -204,11 +214,6 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
               rel[t][v] = TR::add2(crow[lut_c(e)], p2cstrip[int64_t(jj) * RP + lut_p(e)], bj_s[buf][jl]);
             }
         }
-      } else {
-#pragma unroll
-        for (int t = 0; t < NKT; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) rel[t][v] = bj_s[buf][half_major_partner<NKT>(t, g, v)];
       }
 
       // band tiles: each lane group walks its own half of the keys (the tile
@@ -220,7 +225,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
       float rowsum = 0.f;
 #pragma unroll
       for (int t = 0; t < NKT; ++t) {
-        f32x16 S = zero16(), dP = zero16();
+        // far tiles: the per-key terms seed the score accumulator and -Delta
+        // the dP one (P = exp2(fma(S, s log2 e, w)), dS = P dP)
+        f32x16 S = BAND ? zero16() : seq16(&bj_s[buf][half_major_partner<NKT>(t, g, 0)]);
+        f32x16 dP = (BAND || DROP) ? zero16() : splat16(-dlt);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           S = TR::mma(ld_row<TR>(Ks[buf], KP, 32 * t + li, q * KS + g * E), Qf[q], S);
@@ -238,32 +246,34 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int v = 4 * k4 + e;
-              const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
+              const float P = BAND ? fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w)
+                                   : fast_exp2(fmaf(S[v], p.scale_log2, w));
               const float F = r.w[e] >= p.drop_thr ? p.drop_scale : 0.f;
-              dS[v] = P * (dP[v] * F - dlt);
+              dS[v] = P * fmaf(dP[v], F, -dlt);
             }
           }
         } else {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
-            dS[v] = P * (dP[v] - dlt);
+            if constexpr (BAND) {
+              const float P = fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w);
+              dS[v] = P * (dP[v] - dlt);
+            } else {
+              dS[v] = fast_exp2(fmaf(S[v], p.scale_log2, w)) * dP[v];
+            }
           }
         }
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q) {
           const frag sb = TR::pack(&dS[q * E]);
+          // far tiles: this lane's part of the row sum (of the rounded dS the
+          // MFMA uses)
+          if constexpr (!BAND) rowsum = TR::sum(sb, rowsum);
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd)
             dQt[nd] = TR::mma(ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q), sb, dQt[nd]);
         }
-        if constexpr (!BAND) {
-          // far tiles: one row, one sum per tile
-          float rs = 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) rs += dS[v];
-          rowsum += rs + xor32(rs);
-        } else {
+        if constexpr (BAND) {
           // dC2P: this half's keys of the subtile, in order (a block of its
           // own, so the scheduler keeps it apart from the next subtile)
           if (qin) {
@@ -280,6 +290,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
         }
       }
       if constexpr (!BAND) {
+        rowsum += xor32(rowsum);  // the query's two lane halves
         if (qin && g == 0) {
           walk_step<TR, NARROW>(wrow, R, wk, cls == TILE_FAR_LEFT ? R - 1 : 0, rowsum);
           rc = wk.r;
@@ -289,14 +300,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
         walk_merge<TR>(wrow, R, g, wk, rc, sc, qin);
       }
     };
-    if (cls == TILE_BAND)
-      body(BoolC<true>{});
-    else
-      body(BoolC<false>{});
+    body(band_c);
 
     if (kb + 1 < nkb) commit(kb + 1);
     __syncthreads();
-  }
+  };
+  int kb = 0;
+  for (; kb < kb_band; ++kb) iter(kb, BoolC<false>{});
+  for (; kb < kb_right; ++kb) iter(kb, BoolC<true>{});
+  for (; kb < nkb; ++kb) iter(kb, BoolC<false>{});
 
   // close this query's dC2P row, then add the relative term dC2P K_r: the
   // wave's rows are complete once its own stores are (no other wave writes
