@@ -147,11 +147,16 @@ struct WinDma {
   static __device__ __forceinline__ void issue(T* lds, BufView strip, int RP, int row0, int nvalid,
                                                StartFn start_of) {
     const int wave = threadIdx.x >> 6;
+    // the thread index is taken through an empty asm statement so the slot
+    // arithmetic below is redone per call instead of being hoisted out of
+    // the caller's tile loop (where its results would stay live)
+    int tx = int(threadIdx.x);
+    asm volatile("" : "+v"(tx));
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int s0 = k * NT + wave * 64;
       if (s0 >= SLOTS) break;  // wave-uniform
-      const int s = k * NT + int(threadIdx.x);
+      const int s = k * NT + tx;
       if (s < SLOTS) {
         int row, chunk;
         slot(s, row, chunk);

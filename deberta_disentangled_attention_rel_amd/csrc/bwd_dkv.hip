@@ -203,55 +203,66 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
   };
 
   const int nqb = (sq.len + BM - 1) / BM;
+  // the query tiles fall into three contiguous ranges: far-right (tile qb
+  // with qb*BM + BM - 1 - j0 <= d_lo), band, far-left (qb*BM - j0 - BN + 1
+  // >= d_hi); each range runs its own loop, so the far loops carry none of
+  // the band tiles' gathers, windows and walk state
+  const int nr = d_lo + j0 - BM + 1;
+  const int qb_band = min(nqb, nr >= 0 ? nr / BM + 1 : 0);
+  const int qb_left = max(qb_band, min(nqb, (j0 + BN - 1 + d_hi + BM - 1) / BM));
   prefetch(0);
   commit(0);
   wait_vmem();
   __syncthreads();
   if constexpr (AWIN) {
-    if (cls_of(0) == TILE_BAND) {
+    if (qb_band == 0 && qb_left > 0) {
       issue_windows(0, 0);
       wait_vmem();
       __syncthreads();
     }
   }
 
-  for (int qb = 0; qb < nqb; ++qb) {
+  // body of one query tile; mode: 0 far, 1 band (both compiled for that
+  // class alone), 2 decided per tile
+  auto iter = [&](int qb, auto mode_c) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
     const int buf = qb & 1;
     const int i0 = qb * BM;
-    const int cls = cls_of(qb);
-    [[maybe_unused]] const bool next_band = qb + 1 < nqb && cls_of(qb + 1) == TILE_BAND;
+    const bool BAND = MODE == 2 ? (qb >= qb_band && qb < qb_left) : MODE == 1;
+    [[maybe_unused]] const bool next_band = qb + 1 >= qb_band && qb + 1 < qb_left;
     if (qb + 1 < nqb) prefetch(qb + 1);
-    if constexpr (NARROW && !AWIN) {
-      if (cls == TILE_BAND) {
-        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
-        stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
-                                       [&](int r) { return win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - r])) / ES; });
-        if (tid < BM) cb_s[tid] = tid * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][tid]));
-        __syncthreads();
-      }
+    if (NARROW && !AWIN && BAND) {
+      stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+                                    [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
+      stage_window<T, WPW, WPP, 256>(Wp, p2cstrip, RP, BN, j0, sq.len,
+                                     [&](int r) { return win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - r])) / ES; });
+      if (tid < BM) cb_s[tid] = tid * WCP * ES - win_start_bytes<ES>(lut_c(lut_s[buf][tid]));
+      __syncthreads();
     }
 
-    float bj = kbias;
-    if (cls == TILE_FAR_LEFT) bj = b_end0;
-    if (cls == TILE_FAR_RIGHT) bj = b_end1;
+    // far tiles: the per-key P2C term of the tile's class
+    const bool left = qb >= qb_left;
+    const float bj = left ? b_end0 : b_end1;
     // byte base of this key's P2C window row
-    const char* wp = reinterpret_cast<const char*>(Wp) + (AWIN ? WpW::row_offset(jl) : jl * WPP) * ES -
-                     (NARROW && cls == TILE_BAND ? win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - jl])) : 0);
+    [[maybe_unused]] const char* wp =
+        reinterpret_cast<const char*>(Wp) + (AWIN ? WpW::row_offset(jl) : jl * WPP) * ES -
+        (NARROW && BAND ? win_start_bytes<ES>(lut_p(lut_s[buf][NL - 1 - jl])) : 0);
 
     // band tiles: each lane group walks its own half of the queries (the
     // tile is stored half-major, so those are its 16*NQT registers in order)
-    const int r1 = (cls == TILE_BAND && i0 + 16 * NQT < sq.len) ? lut_p(lut_s[buf][16 * NQT - jl + BN - 1]) / (NARROW ? ES : 1)
-                                                                 : -1;
-    WalkHalf wk = walk_begin(g, rc, sc, r1);
+    WalkHalf wk = walk_begin(g, rc, sc, -1);
+    if (BAND) {
+      const int r1 = i0 + 16 * NQT < sq.len ? lut_p(lut_s[buf][16 * NQT - jl + BN - 1]) / (NARROW ? ES : 1) : -1;
+      wk = walk_begin(g, rc, sc, r1);
+    }
     float colsum = 0.f;
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
       // band tiles: the gathered C2P + P2C terms of this subtile's pairs (one
       // block per subtile, so the 16 gathers are in flight together); the
       // per-query C2P value minus the LSE seeds the score accumulator
-      float rel[16];
-      if (cls == TILE_BAND) {
+      [[maybe_unused]] float rel[16];
+      if (BAND) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int il = half_major_partner<NQT>(u, g, v);
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           wd[4 * c + 3] = w3;
         }
       }
-      if (cls == TILE_BAND) {
+      if (BAND) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) P[v] = fast_exp2(fmaf(S[v], p.scale_log2, rel[v]));
       } else {
@@ -331,14 +342,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       for (int q = 0; q < 32 / KS; ++q) {
         const frag pb = TR::pack(&P[q * E]);
         const frag sb = TR::pack(&dS[q * E]);
-        cs = TR::sum(sb, cs);
+        if (!BAND) cs = TR::sum(sb, cs);
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
           dVt[nd] = TR::mma(ld_col<TR>(dOs[buf], QP, 32 * u, 32 * nd, q), pb, dVt[nd]);
           dKt[nd] = TR::mma(ld_col<TR>(Qs[buf], QP, 32 * u, 32 * nd, q), sb, dKt[nd]);
         }
       }
-      if (cls != TILE_BAND) {
+      if (!BAND) {
         // far tiles: one row, one sum per tile
         colsum += cs;
       } else {
@@ -359,12 +370,13 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if constexpr (AWIN) {
       if (next_band) issue_windows(buf ^ 1, i0 + BM);
     }
-    if (cls != TILE_BAND) {
+    if (!BAND) {
       colsum += xor32(colsum);  // the key's two lane halves
       if (jin && g == 0) {
-        walk_step<TR, NARROW>(wrow, R, wk, cls == TILE_FAR_LEFT ? 0 : R - 1, colsum);
-        rc = wk.r;
-        sc = wk.s;
+        WalkHalf wf = walk_begin(0, rc, sc, -1);
+        walk_step<TR, NARROW>(wrow, R, wf, left ? 0 : R - 1, colsum);
+        rc = wf.r;
+        sc = wf.s;
       }
     } else {
       walk_merge<TR>(wrow, R, g, wk, rc, sc, jin);
@@ -372,6 +384,16 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
     if (qb + 1 < nqb) commit(qb + 1);
     wait_vmem();
     __syncthreads();
+  };
+  if constexpr (DROP) {
+    // the dropout bodies need more registers: one loop, the class decided
+    // per tile (with the ranges apart they spill)
+    for (int qb = 0; qb < nqb; ++qb) iter(qb, IntC<2>{});
+  } else {
+    int qb = 0;
+    for (; qb < qb_band; ++qb) iter(qb, IntC<0>{});
+    for (; qb < qb_left; ++qb) iter(qb, IntC<1>{});
+    for (; qb < nqb; ++qb) iter(qb, IntC<0>{});
   }
 
   // close this key's dP2C row, then add the relative term dP2C Q_r (the
