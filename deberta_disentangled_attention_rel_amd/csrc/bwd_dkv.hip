@@ -16,13 +16,19 @@
 //   dV^T += dO^T P,   dK^T += Q^T dS
 //   dP2C[j, r] = sum_{i: delta(j,i) = r} dS[i, j]
 // The strip row of key j is written by an ordered walk over the queries (one
-// step per tile in the far field). dK here is the dS^T Q part; the dP2C Q_r
-// term is added by the relative-gradient GEMM.
+// step per tile in the far field). Once a wave's strip rows are complete, the
+// same kernel adds the relative term dP2C Q_r to its dK accumulators
+// (rel_epilogue) and writes dk.
 //
-// Band tiles gather both relative terms from LDS strip windows (one C2P row
-// per query, one P2C row per key); the table slice holds byte offsets, so a
-// gather address is one add, and the two values and the per-query term are
-// joined with one packed dot product.
+// The query tiles fall into three contiguous ranges (far-right, band,
+// far-left), each with its own loop and its own copy of the tile body (the
+// dropout bodies, which need more registers, keep one loop that decides the
+// class per tile). Far tiles start the score accumulator at the per-query
+// (C2P end - LSE log2e) / (s log2e) and dP at -Delta. Band tiles gather both
+// relative terms from LDS strip windows (one C2P row per query, one P2C row
+// per key); the table slice holds byte offsets, so a gather address is one
+// add, and the two values and the per-key mask term are joined with one
+// packed dot product.
 #include "band.hpp"
 #include "pipe.hpp"
 #include "walk.hpp"

@@ -14,13 +14,17 @@
 //   dQ^T += K^T dS^T
 //   dC2P[i, r] = sum_{j: delta(i,j) = r} dS[i, j]
 // The strip row of query i is written by an ordered walk over the keys (one
-// step per tile in the far field, where the whole tile shares one row). dQ
-// here is the dS K part; the dC2P K_r term is added by the relative-gradient
-// GEMM. No atomics.
+// step per tile in the far field, where the whole tile shares one row). Once
+// a wave's strip rows are complete, the same kernel adds the relative term
+// dC2P K_r to its dQ accumulators (rel_epilogue) and writes dq. No atomics.
 //
-// Band tiles recompute the relative terms as the forward does: C2P from the
+// The key tiles fall into three contiguous ranges (far-left, band,
+// far-right), each with its own loop and its own copy of the tile body. Far
+// tiles start the score accumulator at the per-key P2C end value and dP at
+// -Delta, so P and dS take one FMA, one exp2 and one multiply per pair. Band
+// tiles recompute the relative terms as the forward does: C2P from the
 // query's LDS strip window, P2C straight from the strip in L2, both issued
-// ahead of the score MFMAs. The tile body is compiled once per tile class.
+// ahead of the score MFMAs.
 #include "band.hpp"
 #include "pipe.hpp"
 #include "walk.hpp"
