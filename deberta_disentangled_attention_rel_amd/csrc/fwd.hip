@@ -32,8 +32,8 @@
 // K rows and per-key values are therefore loaded two tiles ahead and V one
 // tile ahead, each into the buffer that the tile two (one) back freed, so two
 // buffers of each suffice and one barrier per tile publishes them. The band
-// range keeps a plain loop (loads one tile ahead, the tile body compiled per
-// tile class), so the gathered relative terms, windows and table slices never
+// range keeps a plain loop (loads one tile ahead, a straight-line band
+// tile body), so the gathered relative terms, windows and table slices never
 // raise the register pressure of the far pipeline. Each range drains its
 // loads before the next one starts.
 #include "band.hpp"
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
   };
 
   // =========================================================================
-  // Band range [kb0, kb1): loads one tile ahead, the tile body compiled once
-  // per tile class.
+  // Band range [kb0, kb1) (every tile of it a band tile): loads one tile
+  // ahead, the tile body straight-line code.
   auto band_range = [&](int kb0, int kb1) {
     auto prefetch = [&](int kb, auto q_c) {
       constexpr int Q = decltype(q_c)::value;
@@ -410,11 +410,9 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       if constexpr (AWIN) {
         // window of the first tile now, row starts of the second for the
         // first iteration
-        if (cls_of(kb0) == TILE_BAND) {
-          win.load_starts(p, i0 - kb0 * BN - BN + 1);
-          win.issue(P ? Wc1 : Wc0, c2pstrip, RP, i0, sq.len);
-        }
-        if (kb0 + 1 < kb1 && cls_of(kb0 + 1) == TILE_BAND) win.load_starts(p, i0 - (kb0 + 1) * BN - BN + 1);
+        win.load_starts(p, i0 - kb0 * BN - BN + 1);
+        win.issue(P ? Wc1 : Wc0, c2pstrip, RP, i0, sq.len);
+        if (kb0 + 1 < kb1) win.load_starts(p, i0 - (kb0 + 1) * BN - BN + 1);
       }
       prefetch(kb0, IntC<P>{});
       commit(kb0, IntC<P>{});
@@ -438,14 +436,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
       // other buffer (free since the last barrier), the row starts of the
       // band tile after it, the next K/V tile
       if constexpr (AWIN) {
-        if (kb + 1 < kb1 && cls_of(kb + 1) == TILE_BAND) win.issue(P ? Wc0 : Wc1, c2pstrip, RP, i0, sq.len);
-        if (kb + 2 < kb1 && cls_of(kb + 2) == TILE_BAND) win.load_starts(p, i0 - (kb + 2) * BN - BN + 1);
+        if (kb + 1 < kb1) win.issue(P ? Wc0 : Wc1, c2pstrip, RP, i0, sq.len);
+        if (kb + 2 < kb1) win.load_starts(p, i0 - (kb + 2) * BN - BN + 1);
       }
       if (kb + 1 < kb1) prefetch(kb + 1, IntC<P ^ 1>{});
 
-      // the score part of the tile body (relative terms, S MFMAs, softmax),
-      // compiled once per tile class as straight-line code; it leaves the
-      // packed probabilities, their row sum and the rescale factor
+      // the score part of the tile body (relative terms, S MFMAs, softmax)
+      // as straight-line code; it leaves the packed probabilities, their row
+      // sum and the rescale factor
       frag pf[NKT][32 / KS];
       float alpha, ls;
       auto body = [&](auto band_c) {
@@ -550,10 +548,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void fwd
             for (int q = 0; q < 32 / KS; ++q) pf[t][q] = TR::pack(&y[t][q * E]);
         }
       };
-      if (cls == TILE_BAND)
-        body(BoolC<true>{});
-      else
-        body(BoolC<false>{});
+      body(BoolC<true>{});
 
       // O^T += V^T P^T after the lazy rescale (same code for both classes,
       // so the accumulators are updated in place)
