@@ -34,7 +34,7 @@ namespace dfa {
 namespace {
 
 template <int DT, int D, int NKT, bool NARROW, bool DROP>
-__global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_kernel(Params p) {
+__global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2 : 1) void dq_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   using frag = typename TR::frag;
@@ -331,7 +331,9 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dq_
 template <int DT, int D, bool NARROW>
 void launch_d(const Params& p, hipStream_t st) {
   dim3 grid(unsigned((p.Lmax + 127) / 128 * p.H * p.nseq));
-  constexpr int NKT = (DT == DF_FP32_T && D == 128) ? 1 : 2;
+  // D=128: 32-key tiles, which fit two work-groups per CU (two waves per
+  // SIMD); a 64-key tile needs one per CU
+  constexpr int NKT = D == 128 ? 1 : 2;
   if (p.drop)
     dq_kernel<DT, D, NKT, NARROW, true><<<grid, 256, 0, st>>>(p);
   else
