@@ -181,6 +181,10 @@ DROP_CASES = {
     "tiny_fp32_L64": (0.5, 1, 2),
     "bf16_big_bucket_odd": (0.25, 99, 4),      # tables that skip rows
     "fp32_D128_wide_bucket": (0.1, 5, 0),
+    # the 16-bit D=128 kernels run 32-key tiles: packed and masked, narrow
+    # and row-skipping tables
+    "fp16_packed_masked_D128": (0.2, 4321, 3),
+    "bf16_D128_wide_bucket_masked": (0.1, 8, 6),
 }
 
 
