@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           }
         }
       }
-      if constexpr (AWIN) {
+      if constexpr (AWIN && MODE != 0) {
         if (u == NQT - 1 && next_band) {
           // this tile's last gather is issued: publish the next tile's table
           // slice and wait for every wave to be done with the windows; the
@@ -374,7 +374,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       }
     }
     if constexpr (AWIN) {
-      if (next_band) issue_windows(buf ^ 1, i0 + BM);
+      if (next_band) {
+        if constexpr (MODE == 0) {
+          // a far tile reads no window: the hand-over waits until its
+          // subtiles are done, so they stay one straight-line block
+          if (tid < NL) lut_s[buf ^ 1][tid] = NARROW ? lreg * ES : lreg;
+          __syncthreads();
+        }
+        issue_windows(buf ^ 1, i0 + BM);
+      }
     }
     if (!BAND) {
       colsum += xor32(colsum);  // the key's two lane halves
