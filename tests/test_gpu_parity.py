@@ -70,6 +70,14 @@ CASES = {
     "fp16_D32_wide_bucket": dict(L=180, H=2, D=32, dtype="fp16", span=100, buckets=128, seed=14),
     "bf16_D128_wide_bucket_masked": dict(lengths=[170, 41, 96], H=2, D=128, span=100, buckets=128, seed=15,
                                          mask_frac=0.2),
+    # the tile ranges (far / band / far) at their edges: span beyond the
+    # sequence (every tile a band tile, no far range), one row in the last
+    # query block with 32-key tiles, and packed lengths on both sides of the
+    # 32-, 64- and 128-row tile edges
+    "bf16_all_band_span_gt_L": dict(L=200, H=2, D=64, span=256, buckets=128, seed=16),
+    "fp16_D128_L129_far": dict(L=129, H=2, D=128, dtype="fp16", span=16, buckets=8, seed=17),
+    "bf16_D128_packed_tile_edges": dict(lengths=[32, 33, 31, 64, 65, 128, 1, 127], H=2, D=128, span=24,
+                                        buckets=8, seed=18, mask_frac=0.1),
 }
 
 
