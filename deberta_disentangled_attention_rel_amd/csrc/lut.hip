@@ -134,15 +134,23 @@ hipError_t launch_reverse_rows(const void* src, void* dst, int H, int R, int D, 
   return hipGetLastError();
 }
 
-// dst[h][d][r] = src[h][r][d] for r < R, 0 for R <= r < RP (the relative
-// rows transposed for the backward kernels' epilogue).
+// The relative rows transposed for the backward kernels' epilogue, in
+// 16-byte chunks: dst[h][r / CE][d][r % CE] = src[h][r][d] for r < R, 0 for
+// R <= r < RP, CE = 16 bytes of elements. A chunk of one row d holds the
+// 16 bytes one lane loads, and the chunks of consecutive rows d are adjacent,
+// so the 32 rows a load instruction reads are one contiguous 512-byte run.
 namespace {
 template <typename T>
 __global__ void transpose_rows_kernel(const T* __restrict__ src, T* __restrict__ dst, int H, int R, int RP, int D) {
+  constexpr int CE = 16 / int(sizeof(T));
   const int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (n >= int64_t(H) * D * RP) return;
-  const int64_t r = n % RP, hd = n / RP;
-  const int64_t d = hd % D, h = hd / D;
+  const int NC = RP / CE;
+  int64_t t = n / CE;
+  const int64_t e = n % CE, d = t % D;
+  t /= D;
+  const int64_t c = t % NC, h = t / NC;
+  const int64_t r = c * CE + e;
   dst[n] = r < R ? src[(h * R + r) * D + d] : T(0);
 }
 }  // namespace

@@ -49,8 +49,8 @@ struct Params {
   void* ends;               // [4][H][T] dtype: c2ps[..][0], c2ps[..][R-1],
                             //   p2cs[..][0], p2cs[..][R-1]
   float* delta;             // [H][T]: rowsum(dO * O)
-  const void* krT;          // [H][D][RP] dtype: k_r transposed (columns >= R zero)
-  const void* qrT;          // [H][D][RP] dtype: the q_r the kernels read, transposed
+  const void* krT;          // [H][RP/CE][D][CE] dtype: k_r transposed in 16-byte chunks (CE elements; columns >= R zero)
+  const void* qrT;          // [H][RP/CE][D][CE] dtype: the q_r the kernels read, transposed the same way
   void* dc2p;               // [H][T][RP] dtype: segmented sums of dS over delta(i,j)
   void* dp2c;               // [H][T][RP] dtype: segmented sums of dS over delta(j,i)
   float* part;              // [2][H][nchunk][R][D] split-K partials

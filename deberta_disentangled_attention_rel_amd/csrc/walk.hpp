@@ -201,8 +201,10 @@ __device__ __forceinline__ constexpr int walk_reg(int k) { return 4 * (k >> 3) +
 // or key, rows m = acc_row(v, g) of d-block nd): dQ^T += K_r^T dC2P^T and
 // dK^T += Q_r^T dP2C^T. `rows` views the work-group's strip rows (`row_off`:
 // byte offset of this lane's partner row; partners past the sequence read
-// zero), `relT` the head's relative rows transposed, [D][RP]. Chunks at or
-// past RP are skipped (they would run into the next row). The strip rows
+// zero), `relT` the head's relative rows transposed in 16-byte chunks,
+// [RP / CE][D][CE] with CE = 16 bytes of elements (a load instruction's 32
+// rows d are then one contiguous run). Chunks at or past RP are skipped (they
+// would run into the next row). The strip rows
 // must be complete and visible: every lane that wrote them has waited for
 // its stores.
 template <typename TR, int ND>
@@ -210,6 +212,7 @@ __device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, in
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, ES = int(sizeof(typename TR::T));
   constexpr int U = 16;  // contraction steps with their loads in flight together
+  constexpr int CE = 16 / ES;  // elements per 16-byte chunk of relT
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
   auto ld = [&](BufView v, int off) -> frag {
     if constexpr (E == 8)
@@ -225,7 +228,8 @@ __device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, in
       const bool in = r < RP;
       b[u] = ld(rows, in ? row_off + r * ES : kBufSkip);
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) a[u][nd] = ld(relT, in ? ((32 * nd + li) * RP + r) * ES : kBufSkip);
+      for (int nd = 0; nd < ND; ++nd)
+        a[u][nd] = ld(relT, in ? (((r / CE) * (ND * 32) + 32 * nd + li) * CE + r % CE) * ES : kBufSkip);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
