@@ -174,16 +174,19 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
     const int buf = kb & 1;
     const int j0 = kb * BN;
     const int cls = decltype(band_c)::value ? TILE_BAND : cls_of(kb);
+    // band tiles: the C2P window is staged before the next tile's loads are
+    // issued (a wave's vector memory operations complete in order, so the
+    // staging's wait then does not wait for those)
+    if constexpr (decltype(band_c)::value && NARROW) {
+      stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
+                                    [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
+      __syncthreads();
+    }
     if (kb + 1 < nkb) prefetch(kb + 1);
 
     // the tile body, compiled once per tile class as straight-line code
     auto body = [&](auto band_c) {
       constexpr bool BAND = decltype(band_c)::value;
-      if constexpr (BAND && NARROW) {
-        stage_window<T, WC, WCP, 256>(Wc, c2pstrip, RP, BM, i0, sq.len,
-                                      [&](int r) { return win_start_bytes<ES>(lut_c(lut_s[buf][r])) / ES; });
-        __syncthreads();
-      }
       const float w = (BAND ? 0.f : (cls == TILE_FAR_LEFT ? a_end1 : a_end0)) - lse2;
 
       // relative terms (log2 domain) of this lane's keys; band tiles gather
