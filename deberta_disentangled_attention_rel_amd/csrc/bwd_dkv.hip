@@ -359,6 +359,14 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         // far tiles: one row, one sum per tile
         colsum += cs;
       } else {
+        if constexpr (AWIN && MODE != 0) {
+          // the next band tile's windows, after this tile's last transposing
+          // reads and before its last walk stores (in the band loop the 16
+          // stores that follow the copy let the tile's end wait for the
+          // copies alone)
+          if (u == NQT - 1 && next_band) issue_windows(buf ^ 1, i0 + BM);
+          __builtin_amdgcn_sched_barrier(0);  // the walk stores stay after the copies
+        }
         // dP2C: this half's queries of the subtile, in order (their rows
         // are read in one batch, so the walk waits on LDS once)
         int wr[16];
@@ -380,8 +388,10 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
           // subtiles are done, so they stay one straight-line block
           if (tid < NL) lut_s[buf ^ 1][tid] = NARROW ? lreg * ES : lreg;
           __syncthreads();
+          issue_windows(buf ^ 1, i0 + BM);
+        } else if (!BAND) {
+          issue_windows(buf ^ 1, i0 + BM);  // (band tiles issued it before their last walk)
         }
-        issue_windows(buf ^ 1, i0 + BM);
       }
     }
     if (!BAND) {
@@ -396,7 +406,15 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       walk_merge<TR>(wrow, R, g, wk, rc, sc, jin);
     }
     if (qb + 1 < nqb) commit(qb + 1);
-    wait_vmem();
+    // this tile's copies (the next query tile, the next band tile's windows)
+    // must land before the barrier publishes them. A tile of the band loop
+    // issues 16 walk stores (one per step, always issued) after its last
+    // copy, and a wave's vector memory operations complete in order, so it
+    // need not wait for those stores
+    if constexpr (AWIN && MODE == 1)
+      wait_vmem_keep<16>();
+    else
+      wait_vmem();
     __syncthreads();
   };
   if constexpr (DROP) {

@@ -292,4 +292,13 @@ struct DmaRows {
 // (vmcnt(0); export and LDS counters left alone).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this thread's vector-memory operations are still
+// outstanding: they complete in issue order, so every one issued before the
+// last N is done (vmcnt(N); bits 3:0 and 15:14 of the count).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 }  // namespace dfa
