@@ -376,8 +376,8 @@ int set_dropout(dfa::Params& prm, const Dropout* d) {
     return fail(DF_ERR_UNSUPPORTED, "fp16 dropout needs dropout_p <= 0.999 (1/(1-p) must stay small in fp16), got %g",
                 double(d->p));
   prm.drop = 1;
-  const double thr = std::floor(double(d->p) * 4294967296.0);
-  prm.drop_thr = thr >= 4294967295.0 ? 0xffffffffu : uint32_t(thr);
+  // p < 1, so floor(p 2^16) <= 65535 fits the 16 bits a pair draws
+  prm.drop_thr = uint32_t(std::floor(double(d->p) * 65536.0));
   prm.drop_scale = float(1.0 / (1.0 - double(d->p)));
   prm.seed_lo = uint32_t(d->seed);
   prm.seed_hi = uint32_t(d->seed >> 32);

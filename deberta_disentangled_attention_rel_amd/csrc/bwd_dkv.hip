@@ -304,25 +304,33 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         dP = TR::mma(ld_row<TR>(dOs[buf], QP, 32 * u + li, q * KS + g * E), Vf[q], dP);
       }
       float P[16], dS[16];
-      [[maybe_unused]] uint32_t wd[16];
+      [[maybe_unused]] uint32_t wd[8];
       if constexpr (DROP) {
-        // This lane's key is word jw % 4 of the call for (query, key group
-        // jw / 4), and the four lanes of a quad hold the four keys of one
-        // group and the same 16 queries. Lane e of the quad computes the
-        // calls of queries 4c + e; a 4 x 4 transpose inside the quad (two
-        // exchange steps) then hands each lane its own word of every call.
-        const int e = lane & 3;
+        // This lane's key takes 16 bits of the call for (query, key block
+        // jw / 8), and the eight lanes 8m .. 8m+7 hold the eight keys of one
+        // block and the same 16 queries (slots v, queries ib + v). Lane e of
+        // the eight computes the calls of slots 2e and 2e + 1 and packs, for
+        // each lane d of the eight, the bits of key d of both calls into one
+        // word (low half slot 2e, high half slot 2e + 1); an 8 x 8 transpose
+        // of those words (an exchange with lane e ^ 4, then a 4 x 4
+        // transpose in each quad) leaves wd[s] = key jw's bits of slots 2s
+        // (low half) and 2s + 1 (high half).
+        const int e = lane & 7;
+        const uint32_t i2 = uint32_t(i0 + ib + 2 * e);
+        const Philox4 r0 = philox4x32_10(uint32_t(jw) >> 3, i2, uint32_t(blk.z * p.H + h), p.drop_off, p.seed_lo,
+                                         p.seed_hi);
+        const Philox4 r1 = philox4x32_10(uint32_t(jw) >> 3, i2 + 1u, uint32_t(blk.z * p.H + h), p.drop_off,
+                                         p.seed_lo, p.seed_hi);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const Philox4 r = philox4x32_10(uint32_t(jw) >> 2, uint32_t(i0 + half_major_partner<NQT>(u, g, 4 * c + e)),
-                                          uint32_t(blk.z * p.H + h), p.drop_off, p.seed_lo, p.seed_hi);
-          uint32_t w0 = r.w[0], w1 = r.w[1], w2 = r.w[2], w3 = r.w[3];
-          quad_transpose(w0, w1, w2, w3, e);
-          wd[4 * c] = w0;
-          wd[4 * c + 1] = w1;
-          wd[4 * c + 2] = w2;
-          wd[4 * c + 3] = w3;
+        for (int k = 0; k < 4; ++k) {
+          // key 2k: low halves of word k, key 2k + 1: high halves
+          wd[2 * k] = (r0.w[k] & 0xFFFFu) | (r1.w[k] << 16);
+          wd[2 * k + 1] = (r0.w[k] >> 16) | (r1.w[k] & 0xFFFF0000u);
         }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xor4_swap(wd[k], wd[k + 4]);
+        quad_transpose(wd[0], wd[1], wd[2], wd[3], e & 3);
+        quad_transpose(wd[4], wd[5], wd[6], wd[7], e & 3);
       }
       if (BAND) {
 #pragma unroll
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
         if constexpr (DROP) {
           // dS = P (F dP - Delta), F = keep / (1 - p); dV takes P keep (the
           // 1 / (1 - p) factor multiplies dV once at the end)
-          const bool keep = wd[v] >= p.drop_thr;
+          const bool keep = (v & 1) ? keep_hi(wd[v >> 1], p.drop_thr) : keep_lo(wd[v >> 1], p.drop_thr);
           dS[v] = P[v] * fmaf(dP[v], keep ? p.drop_scale : 0.f, dlt_s[buf][ib + v]);
           P[v] = keep ? P[v] : 0.f;
         } else {

@@ -243,20 +243,21 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
         }
         float dS[16];
         if constexpr (DROP) {
-          // dS = P (F dP - Delta), F = keep / (1 - p): registers 4k..4k+3
-          // hold four consecutive keys, one Philox call
+          // dS = P (F dP - Delta), F = keep / (1 - p). The keys are
+          // half-major: registers 8c .. 8c+7 hold the eight keys of one
+          // Philox block, so each lane computes its own two calls
+          const int jb = j0 + half_major_partner<NKT>(t, g, 0);  // a multiple of 16
 #pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int j = j0 + half_major_partner<NKT>(t, g, 4 * k4);
-            const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h), p.drop_off,
-                                            p.seed_lo, p.seed_hi);
+          for (int c = 0; c < 2; ++c) {
+            const Philox4 r = philox4x32_10(uint32_t(jb >> 3) + uint32_t(c), uint32_t(iw), uint32_t(blk.z * p.H + h),
+                                            p.drop_off, p.seed_lo, p.seed_hi);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * k4 + e;
+            for (int e = 0; e < 8; ++e) {
+              const int v = 8 * c + e;
               const float P = BAND ? fast_exp2(fmaf(S[v], p.scale_log2, rel[t][v]) + w)
                                    : fast_exp2(fmaf(S[v], p.scale_log2, w));
-              const float F = r.w[e] >= p.drop_thr ? p.drop_scale : 0.f;
-              dS[v] = P * fmaf(dP[v], F, -dlt);
+              const bool keep = (e & 1) ? keep_hi(r.w[e >> 1], p.drop_thr) : keep_lo(r.w[e >> 1], p.drop_thr);
+              dS[v] = P * fmaf(dP[v], keep ? p.drop_scale : 0.f, -dlt);
             }
           }
         } else {

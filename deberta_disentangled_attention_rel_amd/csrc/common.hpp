@@ -245,9 +245,11 @@ __device__ __forceinline__ uint4 buf_load16(BufView b, int voff, int soff = 0) {
 // (Salmon, Moraes, Dror and Shaw, SC 2011): a round maps counter
 // (c0, c1, c2, c3) and key (k0, k1) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2),
 // hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key grows by (W0, W1) before every
-// round after the first. The pair (query i, key j) of sequence n, head h
-// draws word j % 4 of the call with counter (j / 4, i, n H + h, offset) and
-// key (seed low, seed high) and is kept iff that word >= the threshold.
+// round after the first. One call with counter (j / 8, i, n H + h, offset)
+// and key (seed low, seed high) covers the keys 8m .. 8m+7 of query i of
+// sequence n, head h: key j takes the low (j even) or high (j odd) 16 bits of
+// word (j % 8) / 2, and the pair is kept iff those bits, as an unsigned
+// number, are >= the threshold floor(p 2^16).
 struct Philox4 {
   uint32_t w[4];
 };
@@ -274,6 +276,25 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     c3 = lo0;
   }
   return {{c0, c1, c2, c3}};
+}
+
+// Keep tests of the two keys of one word: the low half compared as a 16-bit
+// number (one SDWA compare), the high half by comparing the whole word with
+// the threshold moved up 16 bits (the low half cannot change that order).
+__device__ __forceinline__ bool keep_lo(uint32_t w, uint32_t thr) { return uint16_t(w) >= uint16_t(thr); }
+__device__ __forceinline__ bool keep_hi(uint32_t w, uint32_t thr) { return w >= (thr << 16); }
+
+// Exchange between lanes l and l ^ 4 inside each group of 8 lanes: lanes with
+// bit 2 clear take `a` of lane l + 4 into `b`, lanes with bit 2 set take `b` of
+// lane l - 4 into `a`. Two DPP row shifts, each writing only the banks (4-lane
+// groups of a 16-lane row) it serves.
+__device__ __forceinline__ void xor4_swap(uint32_t& a, uint32_t& b) {
+  // row_shl:4 (lane l reads l + 4) into banks 0 and 2, row_shr:4 (l reads
+  // l - 4) into banks 1 and 3
+  const uint32_t nb = uint32_t(__builtin_amdgcn_update_dpp(int(b), int(a), 0x104, 0xF, 0x5, false));
+  const uint32_t na = uint32_t(__builtin_amdgcn_update_dpp(int(a), int(b), 0x114, 0xF, 0xA, false));
+  a = na;
+  b = nb;
 }
 
 // 4 x 4 transpose inside each quad of lanes (lanes 4m .. 4m+3): on entry

@@ -48,6 +48,33 @@ constexpr float kMaxSlack = 8.f;
 // Scheduling-group masks (AMDGPU sched_group_barrier).
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
 
+// Dropout of one 32-key subtile of P (lane = query i; register 4b + e holds
+// key jt + 8b + 4g + e, so block b of the subtile's four 8-key blocks has its
+// keys 0..3 in lane group 0 and 4..7 in lane group 1). Lane group g computes
+// the calls of blocks 2g and 2g + 1; v_permlane32_swap (lanes 32..63 of the
+// first operand with lanes 0..31 of the second) swaps words 0, 1 of one
+// group's calls with words 2, 3 of the other's, which leaves each lane the two
+// words of its four keys in every block. Dropped values become 0.
+__device__ __forceinline__ void drop_subtile(float (&y)[16], int jt, int g, uint32_t i, uint32_t stream,
+                                             const Params& p) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const Philox4 r = philox4x32_10(uint32_t(jt >> 3) + uint32_t(2 * g + c), i, stream, p.drop_off, p.seed_lo,
+                                    p.seed_hi);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(r.w[0], r.w[2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(r.w[1], r.w[3], false, false);
+    // s*[0]: block c, s*[1]: block 2 + c
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = 4 * (c + 2 * h);
+      y[b] = keep_lo(s0[h], p.drop_thr) ? y[b] : 0.f;
+      y[b + 1] = keep_hi(s0[h], p.drop_thr) ? y[b + 1] : 0.f;
+      y[b + 2] = keep_lo(s1[h], p.drop_thr) ? y[b + 2] : 0.f;
+      y[b + 3] = keep_hi(s1[h], p.drop_thr) ? y[b + 3] : 0.f;
+    }
+  }
+}
+
 template <int DT, int D, int NKT, bool NARROW, bool DROP>
 __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2 : 1) void fwd_kernel(Params p) {
   using TR = Tr<DT>;
@@ -300,23 +327,13 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
         for (int v = 0; v < 16; ++v) y[t][v] = fast_exp2(fmaf(y[t][v], p.scale_log2, -shift));
       if constexpr (DROP) {
         // the row sum is of the undropped P; P V takes the dropped P (kept
-        // or zero, unscaled: 1 / (1 - p) multiplies O once at the end).
-        // Registers 4k..4k+3 of a subtile hold four consecutive keys, one
-        // Philox call.
+        // or zero, unscaled: 1 / (1 - p) multiplies O once at the end)
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
           for (int q = 0; q < 32 / KS; ++q) ls = TR::sum(TR::pack(&y[t][q * E]), ls);
 #pragma unroll
-        for (int t = 0; t < NKT; ++t)
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int j = j0 + 32 * t + acc_row(4 * k4, g);
-            const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h), p.drop_off,
-                                            p.seed_lo, p.seed_hi);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[t][4 * k4 + e] = r.w[e] >= p.drop_thr ? y[t][4 * k4 + e] : 0.f;
-          }
+        for (int t = 0; t < NKT; ++t) drop_subtile(y[t], j0 + 32 * t, g, uint32_t(iw), uint32_t(blk.z * p.H + h), p);
 #pragma unroll
         for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -557,14 +574,7 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
           // P V takes the dropped P (kept or zero, unscaled)
 #pragma unroll
           for (int t = 0; t < NKT; ++t)
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-              const int j = j0 + 32 * t + acc_row(4 * k4, g);
-              const Philox4 r = philox4x32_10(uint32_t(j) >> 2, uint32_t(iw), uint32_t(blk.z * p.H + h),
-                                              p.drop_off, p.seed_lo, p.seed_hi);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) y[t][4 * k4 + e] = r.w[e] >= p.drop_thr ? y[t][4 * k4 + e] : 0.f;
-            }
+            drop_subtile(y[t], j0 + 32 * t, g, uint32_t(iw), uint32_t(blk.z * p.H + h), p);
 #pragma unroll
           for (int t = 0; t < NKT; ++t)
 #pragma unroll

@@ -56,7 +56,7 @@ struct Params {
   float* part;              // [2][H][nchunk][R][D] split-K partials
   // attention-probability dropout (drop = 0: none)
   int drop;
-  uint32_t drop_thr;        // a pair is kept iff its Philox word >= drop_thr
+  uint32_t drop_thr;        // floor(p 2^16): a pair is kept iff its 16 Philox bits >= drop_thr
   float drop_scale;         // 1 / (1 - p)
   uint32_t seed_lo, seed_hi, drop_off;
   int nchunk;

@@ -198,9 +198,11 @@ int df_attn_bwd(const df_attn_shape* shape,
  * rather than reading a saved one). After the softmax each probability is kept with probability
  * 1 - dropout_p and scaled by 1 / (1 - dropout_p), or set to 0; the LSE is
  * that of the undropped scores. The mask is a function of (seed, offset) and
- * the pair: for sequence n, head h, local query i and local key j, word j % 4
- * of Philox4x32-10 with counter (j / 4, i, n * num_heads + h, offset) and key
- * (seed mod 2^32, seed >> 32) keeps the pair iff it is >= floor(p * 2^32).
+ * the pair: for sequence n, head h, local query i and local key j, the call
+ * of Philox4x32-10 with counter (j / 8, i, n * num_heads + h, offset) and key
+ * (seed mod 2^32, seed >> 32) covers keys 8 (j / 8) .. 8 (j / 8) + 7; key j
+ * takes the low (j even) or high (j odd) 16 bits of its word (j % 8) / 2 and
+ * keeps the pair iff they are >= floor(p * 2^16).
  * The backward must be called with the forward's (dropout_p, seed, offset).
  * Arguments otherwise as df_attn_fwd / df_attn_bwd; dropout_p must be in
  * [0, 1) (DF_ERR_INVALID otherwise; for DF_FP16 at most 0.999, else

@@ -13,11 +13,14 @@ round after the first; 10 rounds.
 Attention dropout (DisentangledFlash 1.1.1 page, "Status": the fused kernels
 apply dropout to the attention probabilities, and the backward recomputes the
 mask from the Philox counter rather than saving it). The pages do not
-fix the counter layout; the reading used here (and by the kernels):
-for sequence n of the batch, head h, local query i and local key j,
-    counter = (j // 4, i, n * H + h, offset),  key = (seed mod 2^32, seed >> 32)
-and the pair is kept iff word j % 4 of the output is >= floor(p * 2^32); kept
-probabilities are scaled by 1 / (1 - p).
+fix the counter layout or how many random bits a pair takes; the reading
+used here (and by the kernels): for sequence n of the batch, head h, local
+query i and local key j, one call covers the eight keys 8m .. 8m+7 of a query,
+    counter = (j // 8, i, n * H + h, offset),  key = (seed mod 2^32, seed >> 32),
+and key j takes 16 bits of it: word (j % 8) // 2 of the output, its low half
+for even j and its high half for odd j. The pair is kept iff those 16 bits,
+read as an unsigned number, are >= floor(p * 2^16); kept probabilities are
+scaled by 1 / (1 - p).
 """
 from __future__ import annotations
 
@@ -48,10 +51,10 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    """Words >= this value keep their pair (p in [0, 1))."""
+    """16-bit values >= this keep their pair (p in [0, 1))."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(np.floor(p * 4294967296.0))
+    return int(np.floor(p * 65536.0))
 
 
 def keep_mask(p: float, seed: int, offset: int, n: int, h: int, H: int, L: int) -> np.ndarray:
@@ -60,8 +63,10 @@ def keep_mask(p: float, seed: int, offset: int, n: int, h: int, H: int, L: int) 
     if L == 0:  # an empty sequence has no pairs
         return np.zeros((0, 0), dtype=bool)
     i = np.arange(L, dtype=np.uint64)[:, None]
-    jg = np.arange((L + 3) // 4, dtype=np.uint64)[None, :]
-    words = philox4x32_10(jg, i, np.uint64(n * H + h), np.uint64(offset & _U32), seed & _U32,
+    jb = np.arange((L + 7) // 8, dtype=np.uint64)[None, :]
+    words = philox4x32_10(jb, i, np.uint64(n * H + h), np.uint64(offset & _U32), seed & _U32,
                           (seed >> 32) & _U32)
-    w = np.stack(words, axis=-1).reshape(L, -1)[:, :L]  # word j % 4 of group j // 4
-    return w >= np.uint64(thr)
+    w = np.stack(words, axis=-1)  # [L, blocks, 4]
+    halves = np.stack([w & np.uint64(0xFFFF), w >> np.uint64(16)], axis=-1)  # [L, blocks, 4, 2]
+    bits16 = halves.reshape(L, -1)[:, :L]  # key j: half j % 2 of word (j % 8) // 2 of block j // 8
+    return bits16 >= np.uint64(thr)

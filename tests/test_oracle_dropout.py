@@ -63,8 +63,13 @@ def test_keep_fraction_and_stream_separation():
     n = m.size
     frac = m.mean()
     assert abs(frac - (1 - p)) <= 5 * np.sqrt(p * (1 - p) / n)
-    # every 4-key group uses one call: its four keys are still independent bits
-    assert abs(m[:, 0::4].mean() - m[:, 3::4].mean()) <= 10 * np.sqrt(p * (1 - p) / (n / 4))
+    # every 8-key block uses one call, two keys per output word: each key
+    # position of the block, and the low and high half of a word, keeps 1 - p
+    for pos in range(8):
+        assert abs(m[:, pos::8].mean() - (1 - p)) <= 6 * np.sqrt(p * (1 - p) / (n / 8)), pos
+    # the two keys of one word decide independently: P(both kept) = (1 - p)^2
+    both = (m[:, 0:L - 1:2] & m[:, 1::2]).mean()
+    assert abs(both - (1 - p) ** 2) <= 6 * np.sqrt((1 - p) ** 2 * (1 - (1 - p) ** 2) / (n / 2))
     for other in (philox.keep_mask(p, 43, 0, 0, 1, H, L), philox.keep_mask(p, 42, 1, 0, 1, H, L),
                   philox.keep_mask(p, 42, 0, 0, 2, H, L), philox.keep_mask(p, 42, 0, 1, 1, H, L)):
         agree = (other == m).mean()
