@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
   const uint32_t seq_bytes = uint32_t(sq.len) * uint32_t(p.ts * ES);
   const BufView kview = buf_view(kbase, seq_bytes), vview = buf_view(vbase, seq_bytes);
   [[maybe_unused]] DmaRows<T, BN, D, KP, 256> kdma;
-  [[maybe_unused]] DmaRows<T, BN, D, VP, 256> vdma;
+  [[maybe_unused]] DmaRows<T, BN, D, VP, 256, false, true> vdma;  // rows interleaved for the transposing reads
   if constexpr (DMA) {
     kdma.init(p.ts);
     vdma.init(p.ts);
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q)
 #pragma unroll
-          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vc, VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
+          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR, DMA>(Vc, VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
       finish(IntC<P ^ 1>{}, acc);
       if constexpr (ES == 2) {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 6, 0);
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q)
 #pragma unroll
-          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR>(Vc, VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
+          for (int nd = 0; nd < ND; ++nd) O[nd] = TR::mma(ld_col<TR, DMA>(Vc, VP, 32 * t, 32 * nd, q), pf[t][q], O[nd]);
       l = l * alpha + ls;
 
       if (kb + 1 < kb1) commit(kb + 1, IntC<P ^ 1>{});

@@ -28,16 +28,26 @@ __device__ __forceinline__ typename TR::frag ld_row(const typename TR::T* X, int
   return TR::ld(X + row * P + col);
 }
 
+// Row interleave inside each group of 8 LDS rows: row 4h + m (h < 2, m < 4)
+// sits at slot 2m + h. A transposing read takes rows 4h .. 4h+3 of a group in
+// one half-wave (64 bytes of each); interleaved, they sit at slots 2m + h,
+// whose pieces fall on disjoint banks of the 64 for the V / Q / dO pitch
+// (D + 16 elements), where consecutive rows wrap onto each other.
+__device__ __forceinline__ constexpr int swz8_slot(int row) { return (row & ~7) | ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ constexpr int swz8_row(int slot) { return (slot & ~7) | ((slot & 1) << 2) | ((slot >> 1) & 3); }
+
 // Column fragment for contraction step q: rows r0 + 16q + {4g..4g+3, 8+4g..8+4g+3}
 // (16-bit, two transposing reads) or row r0 + acc_row(q, g) (fp32), column
-// c0 + (lane % 32).
-template <typename TR>
+// c0 + (lane % 32). SWZ: the 16-bit tile's rows are interleaved (swz8_slot;
+// r0 a multiple of 8).
+template <typename TR, bool SWZ = false>
 __device__ __forceinline__ typename TR::frag ld_col(const typename TR::T* X, int P, int r0, int c0, int q) {
   using T = typename TR::T;
   const int lane = threadIdx.x & 63;
   if constexpr (TR::E == 8) {
     const int b = lane >> 4, s = lane & 15;
-    const T* a = X + (r0 + 16 * q + 4 * (b >> 1) + (s >> 2)) * P + c0 + 16 * (b & 1) + 4 * (s & 3);
+    const int rr = SWZ ? 2 * (s >> 2) + (b >> 1) : 4 * (b >> 1) + (s >> 2);
+    const T* a = X + (r0 + 16 * q + rr) * P + c0 + 16 * (b & 1) + 4 * (s & 3);
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 8 * P));
@@ -252,7 +262,8 @@ struct DmaTile {
 // offset, so issuing a tile takes no address arithmetic. Rows at or past the
 // end of the view, and the row-padding chunks, load zeros without touching
 // memory (the hardware range check).
-template <typename T, int ROWS, int D, int P, int NT, bool HALF_MAJOR = false>
+// SWZ interleaves the rows (LDS slot n holds logical row swz8_row(n)).
+template <typename T, int ROWS, int D, int P, int NT, bool HALF_MAJOR = false, bool SWZ = false>
 struct DmaRows {
   static constexpr int PC = P / 8, NC = D / 8;
   static constexpr int SLOTS = ROWS * PC;
@@ -265,7 +276,8 @@ struct DmaRows {
     for (int k = 0; k < NI; ++k) {
       const int s = k * NT + int(threadIdx.x);
       const int slot = s / PC, c = s % PC;
-      const int row = HALF_MAJOR ? half_major_at<ROWS / 32>(slot) : slot;
+      const int lrow = SWZ ? swz8_row(slot) : slot;
+      const int row = HALF_MAJOR ? half_major_at<ROWS / 32>(lrow) : lrow;
       voff[k] = (s < SLOTS && c < NC) ? int(row * ts * int64_t(sizeof(T))) + c * 16 : kBufSkip;
     }
   }
