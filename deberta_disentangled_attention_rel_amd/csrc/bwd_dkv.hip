@@ -354,13 +354,20 @@ __global__ __launch_bounds__(256, (D <= 64 && DT != DF_FP32_T) ? 2 : 1) void dkv
       float cs = 0.f;  // far tiles: this lane's part of the column sum (of the rounded dS the MFMA uses)
 #pragma unroll
       for (int q = 0; q < 32 / KS; ++q) {
+        // the step's dO and Q fragments first, so their reads share one wait
+        frag fo[ND], fq[ND];
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          fo[nd] = ld_col<TR>(dOs[buf], QP, 32 * u, 32 * nd, q);
+          fq[nd] = ld_col<TR>(Qs[buf], QP, 32 * u, 32 * nd, q);
+        }
         const frag pb = TR::pack(&P[q * E]);
         const frag sb = TR::pack(&dS[q * E]);
         if (!BAND) cs = TR::sum(sb, cs);
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
-          dVt[nd] = TR::mma(ld_col<TR>(dOs[buf], QP, 32 * u, 32 * nd, q), pb, dVt[nd]);
-          dKt[nd] = TR::mma(ld_col<TR>(Qs[buf], QP, 32 * u, 32 * nd, q), sb, dKt[nd]);
+          dVt[nd] = TR::mma(fo[nd], pb, dVt[nd]);
+          dKt[nd] = TR::mma(fq[nd], sb, dKt[nd]);
         }
       }
       if (!BAND) {

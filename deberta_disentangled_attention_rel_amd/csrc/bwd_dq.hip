@@ -271,6 +271,12 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
             }
           }
         }
+        // the subtile's K fragments first, so their reads share the waits
+        frag fk[32 / KS][ND];
+#pragma unroll
+        for (int q = 0; q < 32 / KS; ++q)
+#pragma unroll
+          for (int nd = 0; nd < ND; ++nd) fk[q][nd] = ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q);
 #pragma unroll
         for (int q = 0; q < 32 / KS; ++q) {
           const frag sb = TR::pack(&dS[q * E]);
@@ -278,8 +284,7 @@ __global__ __launch_bounds__(256, (DT != DF_FP32_T && (D <= 64 || NKT == 1)) ? 2
           // MFMA uses)
           if constexpr (!BAND) rowsum = TR::sum(sb, rowsum);
 #pragma unroll
-          for (int nd = 0; nd < ND; ++nd)
-            dQt[nd] = TR::mma(ld_col<TR>(Ks[buf], KP, 32 * t, 32 * nd, q), sb, dQt[nd]);
+          for (int nd = 0; nd < ND; ++nd) dQt[nd] = TR::mma(fk[q][nd], sb, dQt[nd]);
         }
         if constexpr (BAND) {
           // dC2P: this half's keys of the subtile, in order (a block of its

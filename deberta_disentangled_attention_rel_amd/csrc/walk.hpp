@@ -206,12 +206,16 @@ __device__ __forceinline__ constexpr int walk_reg(int k) { return 4 * (k >> 3) +
 // rows d are then one contiguous run). Chunks at or past RP are skipped (they
 // would run into the next row). The strip rows
 // must be complete and visible: every lane that wrote them has waited for
-// its stores.
+// its stores. The contraction runs in batches of U steps, double-buffered:
+// a batch's loads go out before the previous batch's MFMAs (a scheduling
+// barrier keeps them there), so each batch waits only for loads issued a
+// batch earlier. Batches past RP load zeros without touching memory (range
+// check) and add nothing, so every batch's loads are issued unconditionally.
 template <typename TR, int ND>
 __device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, int row_off, BufView relT, int RP) {
   using frag = typename TR::frag;
   constexpr int E = TR::E, KS = TR::KS, ES = int(sizeof(typename TR::T));
-  constexpr int U = 16;  // contraction steps with their loads in flight together
+  constexpr int U = ND <= 2 ? 4 : 2;  // steps per batch (two batches of U (1 + ND) fragments live)
   constexpr int CE = 16 / ES;  // elements per 16-byte chunk of relT
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
   auto ld = [&](BufView v, int off) -> frag {
@@ -220,8 +224,7 @@ __device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, in
     else
       return buf_load<typename TR::T>(v, off, 0);
   };
-  for (int r0 = 0; r0 < RP; r0 += U * KS) {
-    frag b[U], a[U][ND];
+  auto load = [&](frag (&b)[U], frag (&a)[U][ND], int r0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = r0 + u * KS + g * E;
@@ -231,10 +234,24 @@ __device__ __forceinline__ void rel_epilogue(f32x16 (&acc)[ND], BufView rows, in
       for (int nd = 0; nd < ND; ++nd)
         a[u][nd] = ld(relT, in ? (((r / CE) * (ND * 32) + 32 * nd + li) * CE + r % CE) * ES : kBufSkip);
     }
+  };
+  auto mma = [&](const frag (&b)[U], const frag (&a)[U][ND]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a[u][nd], b[u], acc[nd]);
+  };
+  frag b0[U], a0[U][ND], b1[U], a1[U][ND];
+  load(b0, a0, 0);
+  for (int r0 = 0; r0 < RP; r0 += 2 * U * KS) {
+    load(b1, a1, r0 + U * KS);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(b0, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b0, a0, r0 + 2 * U * KS);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(b1, a1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
