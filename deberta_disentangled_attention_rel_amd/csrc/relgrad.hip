@@ -7,10 +7,12 @@
 //
 // (The per-token terms s * dC2P K_r and s * dP2C Q_r are added by the dQ and
 // dK/dV kernels themselves, at the end of each work-group.) The GEMM stages
-// row-major tiles with coalesced 16-byte loads, prefetching the next tile
-// into registers while the current one is multiplied (double-buffered LDS,
-// one barrier per step); operands that run down the rows are read with
-// transposing LDS reads. The token sums are split into fixed chunks; each
+// row-major tiles with coalesced 16-byte loads, prefetched into registers two
+// token blocks ahead (two register sets in turn; double-buffered LDS, one
+// barrier per step); operands that run down the rows are read with
+// transposing LDS reads. The loads are range-checked buffer loads over the
+// chunk's rows, issued unconditionally, so the wait before a block's LDS
+// store leaves the next block's loads in flight. The token sums are split into fixed chunks; each
 // chunk's [R, D] partial is written to the workspace and a second kernel adds
 // the chunks in index order. No atomics; the chunking depends only on the
 // shape.
@@ -19,6 +21,49 @@
 namespace dfa {
 
 namespace {
+
+// A ROWS x COLS tile staged through registers: each thread's 16-byte chunks
+// have fixed byte offsets in the view (init); a tile's first-row byte offset
+// is added to them, so the whole per-lane offset is range-checked and rows
+// past the view load zero without touching memory.
+template <typename T, int ROWS, int COLS, int NT>
+struct BufTile {
+  static constexpr int CH = 16 / int(sizeof(T)), NC = COLS / CH, CHUNKS = ROWS * NC;
+  static_assert(CHUNKS % NT == 0, "every thread owns whole chunks");
+  static constexpr int PER = CHUNKS / NT;
+  uint4 r[PER];
+  int voff[PER];
+  __device__ __forceinline__ void init(int ld, int col0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int it = int(threadIdx.x) + u * NT;
+      voff[u] = ((it / NC) * ld + col0 + (it % NC) * CH) * int(sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void load(BufView v, int boff) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) r[u] = buf_load16(v, voff[u] + boff);
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int it = int(threadIdx.x) + u * NT;
+      {
+        const int off = (it / NC) * P + (it % NC) * CH;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint4*>(lds + off) = r[u];
+        } else {
+          float* d = reinterpret_cast<float*>(lds) + off;
+          d[0] = __uint_as_float(r[u].x);
+          d[1] = __uint_as_float(r[u].y);
+          d[2] = __uint_as_float(r[u].z);
+          d[3] = __uint_as_float(r[u].w);
+        }
+      }
+    }
+  }
+};
 
 // Split-K partials of dk_r (which = 0: dC2P^T Q) and dq_r (which = 1: dP2C^T K).
 // Workgroup: 128 strip rows r (4 waves x 32) x all D columns, over one chunk
@@ -43,37 +88,54 @@ __global__ __launch_bounds__(256) void dw_kernel(Params p) {
   const int64_t c0 = int64_t(chunk) * p.chunk_tokens;
   const int64_t c1 = c0 + p.chunk_tokens < p.T ? c0 + p.chunk_tokens : p.T;
 
-  // next token block in registers while the current one is multiplied
-  Tile2D<T, TK, RM, 256> gt;
-  Tile2D<T, TK, D, 256> xt;
   f32x16 acc[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) acc[nd] = zero16();
-  if (c0 < c1) {
-    gt.load(G, RP, c0, c1, r0, RP);
-    xt.load(X, p.ts, c0, c1, 0, D);
-    gt.template store<GP>(Gs[0]);
-    xt.template store<XP>(Xs[0]);
+  // views of the chunk's token rows: rows at or past c1 read zero (strip
+  // columns past RP only feed output rows that are never written)
+  const int nt = int(c1 - c0);
+  const BufView gv = buf_view(G + c0 * RP, uint32_t(nt > 0 ? nt : 0) * uint32_t(RP) * uint32_t(sizeof(T)));
+  const BufView xv = buf_view(X + c0 * p.ts, uint32_t(nt > 0 ? nt : 0) * uint32_t(p.ts) * uint32_t(sizeof(T)));
+  const int gstep = TK * RP * int(sizeof(T)), xstep = TK * int(p.ts) * int(sizeof(T));
+  // token blocks two ahead in registers, the two register sets in turn
+  BufTile<T, TK, RM, 256> ga, gb;
+  BufTile<T, TK, D, 256> xa, xb;
+  ga.init(RP, r0);
+  gb.init(RP, r0);
+  xa.init(int(p.ts), 0);
+  xb.init(int(p.ts), 0);
+  const int nk = nt > 0 ? (nt + TK - 1) / TK : 0;
+  if (nk > 0) {
+    ga.load(gv, 0);
+    xa.load(xv, 0);
+    ga.template store<GP>(Gs[0]);
+    xa.template store<XP>(Xs[0]);
+    ga.load(gv, gstep);  // block 1 (zeros past the chunk)
+    xa.load(xv, xstep);
   }
   __syncthreads();
-  int buf = 0;
-  for (int64_t tk = c0; tk < c1; tk += TK, buf ^= 1) {
-    const bool more = tk + TK < c1;
-    if (more) {
-      gt.load(G, RP, tk + TK, c1, r0, RP);
-      xt.load(X, p.ts, tk + TK, c1, 0, D);
-    }
+  // step k: LDS buffer k % 2 holds block k, `cur` holds block k + 1 in
+  // flight; block k + 2 goes into `nxt`, and `cur` is stored after the
+  // MFMAs. Blocks past the chunk are zeros and add nothing, so the steps run
+  // in pairs without conditions (the loop body has no branch that would
+  // split the two register sets)
+  auto step = [&](int k, int buf, auto& cur_g, auto& cur_x, auto& nxt_g, auto& nxt_x) {
+    nxt_g.load(gv, (k + 2) * gstep);
+    nxt_x.load(xv, (k + 2) * xstep);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs and the stores
 #pragma unroll
     for (int q = 0; q < TK / KS; ++q) {
       const auto a = ld_col<TR>(Gs[buf], GP, 0, 32 * wave, q);
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) acc[nd] = TR::mma(a, ld_col<TR>(Xs[buf], XP, 0, 32 * nd, q), acc[nd]);
     }
-    if (more) {
-      gt.template store<GP>(Gs[buf ^ 1]);
-      xt.template store<XP>(Xs[buf ^ 1]);
-    }
+    cur_g.template store<GP>(Gs[buf ^ 1]);
+    cur_x.template store<XP>(Xs[buf ^ 1]);
     __syncthreads();
+  };
+  for (int k = 0; k < nk; k += 2) {
+    step(k, 0, ga, xa, gb, xb);
+    step(k + 1, 1, gb, xb, ga, xa);
   }
   float* part = p.part + ((int64_t(which) * p.H + h) * p.nchunk + chunk) * int64_t(R) * D;
 #pragma unroll
