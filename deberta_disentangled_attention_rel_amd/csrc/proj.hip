@@ -10,11 +10,15 @@
 //
 // Work-group: a 128 x 128 tile of Y, 4 waves as 2 x 2 blocks of 64 x 64
 // (2 x 2 MFMA 32x32x16 accumulators each), the contraction in 64-wide steps.
-// Both operands are K-contiguous rows, so A and W tiles are copied row-major
-// into LDS by buffer LDS-DMA (fixed per-thread offsets, the step's column as
-// the scalar offset; rows past the matrix and columns past E load zero) one
-// step ahead into the other of two buffers, and both fragments are plain
-// 16-byte row reads. Work-groups are renumbered so that each XCD runs a
+// Both operands are K-contiguous rows, so A and W tiles are staged row-major
+// in LDS (two buffers) and both fragments are plain 16-byte row reads. The
+// tiles go through registers two steps ahead (two register sets in turn):
+// each thread's 16-byte chunks have fixed offsets, the step's column is added
+// to them, rows past the matrix read zero (range check) and columns past the
+// contraction are sent past the view by a select, so every load is
+// unconditional and a step's LDS stores wait only for the loads of the step
+// before (one step of copies in flight, as LDS-DMA into two buffers allows,
+// left the steps waiting on memory latency). Work-groups are renumbered so that each XCD runs a
 // contiguous range of tiles, column tile fastest: the tiles of one row block
 // share its A rows in that XCD's L2.
 #include "pipe.hpp"
@@ -25,37 +29,25 @@ namespace {
 
 constexpr int PBM = 128, PBN = 128, PBK = 64, PP = PBK + 8;  // tile and LDS row pitch (elements)
 
-// One operand tile (128 rows x 64 columns) per step: slot s = row * 9 + chunk,
-// chunk 8 is row padding and never loaded.
-struct ProjDma {
-  static constexpr int PC = PP / 8, SLOTS = PBM * PC, NI = (SLOTS + 255) / 256;
-  int voff[NI];  // byte offset of this thread's chunk in the view, or kBufSkip
-  int col[NI];   // element column of the chunk within a step (>= PBK: padding)
-
-  __device__ __forceinline__ void init(int ld_bytes) {
+// One operand tile (128 rows x 64 columns) of a step in registers: chunk
+// u of thread t is row (t + 256u) / 8, columns 8 ((t + 256u) % 8) .. + 7.
+struct ProjRegs {
+  static constexpr int PER = PBM * (PBK / 8) / 256;
+  uint4 r[PER];
+  __device__ __forceinline__ static int row_of(int u) { return (int(threadIdx.x) + 256 * u) / (PBK / 8); }
+  __device__ __forceinline__ static int col_of(int u) { return ((int(threadIdx.x) + 256 * u) % (PBK / 8)) * 8; }
+  // columns k0 .. k0 + 63 of the view's rows (row stride ld elements);
+  // columns at or past K read zero
+  __device__ __forceinline__ void load(BufView b, int ld, int k0, int K) {
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int s = k * 256 + int(threadIdx.x);
-      const int row = s / PC, c = s % PC;
-      col[k] = c < PBK / 8 ? c * 8 : PBK;
-      voff[k] = (s < SLOTS && c < PBK / 8) ? row * ld_bytes + c * 16 : kBufSkip;
+    for (int u = 0; u < PER; ++u) {
+      const int c = k0 + col_of(u);
+      r[u] = buf_load16(b, c < K ? (row_of(u) * ld + c) * 2 : kBufSkip);
     }
   }
-  // columns k0 .. k0 + 63 of the view's rows; columns at or past K read zero
-  __device__ __forceinline__ void issue(uint16_t* lds, BufView b, int k0, int K) const {
-    const int wave = threadIdx.x >> 6;
+  __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int s0 = k * 256 + wave * 64;
-      if (s0 >= SLOTS) break;  // wave-uniform
-      if (k * 256 + int(threadIdx.x) < SLOTS) {
-        const int vo = k0 + col[k] < K ? voff[k] : kBufSkip;
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)(lds + s0 * 8), 16,
-                                                 vo, k0 * 2, 0, 0);
-#endif
-      }
-    }
+    for (int u = 0; u < PER; ++u) *reinterpret_cast<uint4*>(lds + row_of(u) * PP + col_of(u)) = r[u];
   }
 };
 
@@ -85,10 +77,6 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
   const T* W = (const T*)p.w + int64_t(n0) * p.ldw;
   const BufView av = buf_view(A, uint32_t(min(PBM, p.M - m0)) * uint32_t(p.lda) * 2u);
   const BufView wv = buf_view(W, uint32_t(min(PBN, p.N - n0)) * uint32_t(p.ldw) * 2u);
-  ProjDma adma, wdma;
-  adma.init(p.lda * 2);
-  wdma.init(p.ldw * 2);
-
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -96,16 +84,23 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
   const int nk = K > kb ? (K - kb + PBK - 1) / PBK : 0;
-  adma.issue(As[0], av, kb, K);
-  wdma.issue(Bs[0], wv, kb, K);
-  wait_vmem();
+  ProjRegs ra0, rb0, ra1, rb1;
+  if (nk > 0) {
+    ra0.load(av, p.lda, kb, K);
+    rb0.load(wv, p.ldw, kb, K);
+    ra0.store(As[0]);
+    rb0.store(Bs[0]);
+    ra0.load(av, p.lda, kb + PBK, K);  // step 1 (zeros past K)
+    rb0.load(wv, p.ldw, kb + PBK, K);
+  }
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      adma.issue(As[buf ^ 1], av, kb + (kt + 1) * PBK, K);
-      wdma.issue(Bs[buf ^ 1], wv, kb + (kt + 1) * PBK, K);
-    }
+  // step kt: LDS buffer kt % 2 holds step kt, `cur` step kt + 1 in flight;
+  // step kt + 2 goes into `nxt`. Steps past nk read zeros and add nothing,
+  // so the steps run in pairs without conditions.
+  auto step = [&](int kt, int buf, ProjRegs& cur_a, ProjRegs& cur_b, ProjRegs& nxt_a, ProjRegs& nxt_b) {
+    nxt_a.load(av, p.lda, kb + (kt + 2) * PBK, K);
+    nxt_b.load(wv, p.ldw, kb + (kt + 2) * PBK, K);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs and the stores
     const T* a_s = reinterpret_cast<const T*>(As[buf]);
     const T* b_s = reinterpret_cast<const T*>(Bs[buf]);
 #pragma unroll
@@ -120,8 +115,13 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = TR::mma(af[i], bf[j], acc[i][j]);
     }
-    wait_vmem();
+    cur_a.store(As[buf ^ 1]);
+    cur_b.store(Bs[buf ^ 1]);
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, 0, ra0, rb0, ra1, rb1);
+    step(kt + 1, 1, ra1, rb1, ra0, rb0);
   }
 
   // lane: column n = n0 + wn*64 + 32j + li; register v: row m0 + wm*64 + 32i + acc_row(v, g)
