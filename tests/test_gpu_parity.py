@@ -225,6 +225,96 @@ def test_dropout_parity(name):
     assert not bad, (errs, bad)
 
 
+def _onehot_rows(lengths, H, D):
+    """[T, H, D] float64 with row t = e_i, i = t's position in its sequence
+    (every length <= D)."""
+    x = np.zeros((sum(lengths), H, D))
+    st = 0
+    for n in lengths:
+        i = np.arange(n)
+        x[st + i, :, i] = 1.0
+        st += n
+    return x
+
+
+@pytest.mark.parametrize("D,lengths", [(64, [64, 37, 1, 9, 16, 63, 8]), (128, [128, 77, 1, 33, 96, 8, 9])])
+def test_dropout_mask_bits(D, lengths):
+    """Each kernel's keep decisions against the oracle's mask, pair by pair
+    (a rel-L2 over a whole tensor could hide a few wrong pairs).
+
+    Forward and dK/dV: with V and dO one-hot by position in the sequence,
+    O[i, j] = P_ij F_ij / (1 - p) and dV[j, i] = P_ij F_ij / (1 - p), so their
+    zero patterns are the two kernels' masks. dQ: with K and V one-hot and
+    the relative rows zero, dQ[i, j] = s dS_ij with dS_ij = P_ij (F_ij dP_ij /
+    (1 - p) - Delta_i), dP_ij = dO_i[j]; each element lies next to the value
+    for F = 1 or for F = 0, decided where the two differ well beyond bf16
+    rounding."""
+    import deberta_disentangled_attention_rel_amd as df
+    from oracle import philox
+    from parity_util import to_dev
+    H, p, seed, offset = 2, 0.3, 20261203 + D, 5
+    print(f"dropout mask bits D={D} lengths={lengths}", flush=True)
+    inp = _inp(lengths=lengths, H=H, D=D, span=64, buckets=32, seed=21 + D)
+    w = inp.workload
+    oh = _onehot_rows(lengths, H, D)
+    masks = []
+    st = 0
+    for n, L in enumerate(lengths):
+        masks.append([philox.keep_mask(p, seed, offset, n, h, H, L) for h in range(H)])
+    dkw = dict(dropout_p=p, seed=seed, offset=offset)
+
+    # forward and dK/dV
+    for nm in ("v", "dout"):
+        inp.t[nm] = torch.from_numpy(oh).to(inp.t[nm].dtype)
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw, **dkw)
+    g = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out, lse, t["dout"], **kw, **dkw)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    dv = g[2].float().cpu().numpy()
+    st = 0
+    for n, L in enumerate(lengths):
+        for h in range(H):
+            m = masks[n][h]
+            assert np.array_equal(o[st:st + L, h, :L] != 0, m), ("forward", n, h)
+            assert np.array_equal(dv[st:st + L, h, :L].T != 0, m), ("dK/dV", n, h)
+        st += L
+
+    # dQ
+    inp = _inp(lengths=lengths, H=H, D=D, span=64, buckets=32, seed=21 + D)
+    for nm in ("k", "v"):
+        inp.t[nm] = torch.from_numpy(oh).to(inp.t[nm].dtype)
+    for nm in ("q_r", "k_r"):
+        inp.t[nm] = torch.zeros_like(inp.t[nm])
+    t, km, cu = to_dev(inp)
+    out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw, **dkw)
+    g = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out, lse, t["dout"], **kw, **dkw)
+    torch.cuda.synchronize()
+    s = 1.0 / np.sqrt(3.0 * D)
+    q = inp.t["q"].double().numpy()
+    do = inp.t["dout"].double().numpy()
+    o = out.double().cpu().numpy()
+    dq = g[0].double().cpu().numpy()
+    st, decided, total = 0, 0, 0
+    for n, L in enumerate(lengths):
+        for h in range(H):
+            S = s * q[st:st + L, h, :L]  # S_ij = s q_i . e_j
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dP = do[st:st + L, h, :L]  # dO_i . e_j
+            dlt = (do[st:st + L, h, :] * o[st:st + L, h, :]).sum(axis=1, keepdims=True)
+            ds1, ds0 = P * (dP / (1.0 - p) - dlt), P * (-dlt)
+            gq = dq[st:st + L, h, :L] / s
+            ok = np.abs(ds1 - ds0) > 0.1 * (np.abs(ds1) + np.abs(ds0))
+            implied = np.abs(gq - ds1) < np.abs(gq - ds0)
+            assert np.array_equal(implied[ok], masks[n][h][ok]), ("dQ", n, h)
+            decided += int(ok.sum())
+            total += L * L
+        st += L
+    assert decided >= 0.8 * total, (decided, total)
+
+
 # ----------------------------------------------------------------------------
 # structure the method fixes, checked on the GPU's own output: every valid row
 # of dS sums to zero, so sum_r dK_r[h, r, :] = 0 (up to the rounding of the
