@@ -182,7 +182,16 @@ int df_attn_fwd_noalloc(const df_attn_shape* shape,
  * gradients overwrite the outputs (never accumulate). Scores are recomputed
  * from the inputs and lse; the index tables and relative-position strips are
  * recomputed too, unless shape->flags has DF_FLAG_BWD_REUSE_FWD (then they
- * are taken from the forward's workspace, see there). */
+ * are taken from the forward's workspace, see there). For a packed batch
+ * (cu_seqlens) whose grid, the longest sequence's 128-row blocks for every
+ * sequence, is at least 1.5 times total_tokens, the dK/dV and dQ kernels run
+ * side by side: dQ on a second stream of the current device (default
+ * priority; the first such call on a device creates it and two events, kept
+ * until the process ends, so make that call before capturing a graph),
+ * forked from `stream` after the preceding work and joined back before the
+ * relative-gradient kernels, so every result is ordered on `stream` as
+ * usual and is bitwise the same either way. The stream must belong to the
+ * current device. */
 int df_attn_bwd(const df_attn_shape* shape,
                 const void* q, const void* k, const void* v,
                 const void* q_r, const void* k_r,

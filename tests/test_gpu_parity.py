@@ -225,6 +225,40 @@ def test_dropout_parity(name):
     assert not bad, (errs, bad)
 
 
+@pytest.mark.parametrize("name,drop", [("bf16_packed_masked", None), ("fp16_packed_masked_D128", None),
+                                       ("bf16_packed_masked", (0.2, 77, 9))])
+def test_bwd_side_by_side_is_bitwise_serial(name, drop):
+    """Packed batches of uneven sequences run the dK/dV and dQ kernels on two
+    streams; every output must be bitwise the serial order's (the stage
+    profiler forces that order), also twice in a row."""
+    import deberta_disentangled_attention_rel_amd as df
+    from parity_util import to_dev
+    print(f"side by side vs serial {name} dropout={drop}", flush=True)
+    inp = _inp(**CASES[name])
+    w = inp.workload
+    t, km, cu = to_dev(inp)
+    kw = dict(key_mask=km, cu_seqlens=cu, max_seqlen=inp.max_seqlen)
+    if drop:
+        kw.update(dropout_p=drop[0], seed=drop[1], offset=drop[2])
+    out, lse = df.fwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, **kw)
+
+    def bwd():
+        g = df.bwd(t["q"], t["k"], t["v"], t["q_r"], t["k_r"], w.span, w.buckets, out, lse, t["dout"], **kw)
+        torch.cuda.synchronize()
+        return [x.clone() for x in g]
+
+    a1, a2 = bwd(), bwd()
+    df.profile_enable(True)
+    try:
+        b = bwd()
+        df.profile_read()
+    finally:
+        df.profile_enable(False)
+    for n_, x, y, z in zip(("dq", "dk", "dv", "dq_r", "dk_r"), a1, a2, b):
+        assert torch.equal(x, y), n_
+        assert torch.equal(x, z), n_
+
+
 def _onehot_rows(lengths, H, D):
     """[T, H, D] float64 with row t = e_i, i = t's position in its sequence
     (every length <= D)."""
