@@ -489,12 +489,12 @@ int scratch_of_device(hipStream_t st, void** ptr) {
 
 // For packed batches of uneven sequences the backward runs the dK/dV and dQ
 // kernels concurrently: they read the same inputs and write disjoint outputs
-// and strips. Their grids are sized by the longest sequence and each XCD runs
-// a contiguous range of sequences, so the work per XCD is uneven and the
-// other kernel's work-groups fill the idle CUs (packed varlen D=128 bf16:
-// fwd+bwd 7.02 -> 6.05 ms). On full grids the two only compete for the L2
-// (L=8192: the backward 2.41 -> 2.6 ms), so they stay in sequence there. dQ
-// goes on a second stream of the device (default priority, created on the first
+// and strips. Their grids are sized by the longest sequence, which leaves
+// many work-groups short or empty, and the other kernel's work-groups fill
+// the gaps (packed varlen D=128 bf16: fwd+bwd 3.94 -> 3.87 ms). On full
+// grids the two only compete for the L2 (L=8192: the backward 2.41 -> 2.6
+// ms), so they stay in sequence there. dQ goes on a second stream of the
+// device (default priority, created on the first
 // backward and kept until the process ends), forked from and joined back to
 // the caller's stream by events. The fork and the join are enqueued under a
 // lock, and a wait takes the event as recorded at that moment, so calls from

@@ -390,9 +390,13 @@ template <int V> struct IntC {
 // Work-group placement over the 8 XCDs of the chip, each with its own L2.
 // The dispatcher hands consecutive work-group ids to the XCDs in turn;
 // attn_block() renumbers a 1-D grid of nx * H * nseq groups so that every XCD
-// runs one contiguous range of logical blocks (row block fastest, then head,
-// then sequence): the row blocks of one (sequence, head) run together on one
-// XCD and share that head's streamed operands in its L2.
+// runs one contiguous range of logical blocks, row block fastest, then
+// sequence, then head. The row blocks of one (sequence, head) run together on
+// one XCD and share that head's streamed operands in its L2, and every head's
+// work is the same sum over the sequences, so the XCDs get equal shares even
+// when the sequences of a packed batch differ in length (ordered head before
+// sequence, the busiest XCD of an 18-sequence packed batch had 2.3 times the
+// mean work).
 constexpr int kXcds = 8;
 struct AttnBlock {
   int x, h, z;
@@ -401,7 +405,8 @@ __device__ __forceinline__ AttnBlock attn_block(int nx, int H) {
   const int nb = gridDim.x, id = blockIdx.x;
   const int q = nb / kXcds, r = nb % kXcds, xcd = id % kXcds, slot = id / kXcds;
   const int logical = xcd * q + (xcd < r ? xcd : r) + slot;
-  return {logical % nx, (logical / nx) % H, logical / (nx * H)};
+  const int nz = nb / (nx * H);  // sequences
+  return {logical % nx, logical / (nx * nz), (logical / nx) % nz};
 }
 
 // Sequence bounds of blockIdx.z: padded (cu == nullptr) or packed.
