@@ -46,7 +46,7 @@ __device__ __forceinline__ typename TR::frag ld_col(const typename TR::T* X, int
   const int lane = threadIdx.x & 63;
   if constexpr (TR::E == 8) {
     const int b = lane >> 4, s = lane & 15;
-    const int rr = SWZ ? 2 * (s >> 2) + (b >> 1) : 4 * (b >> 1) + (s >> 2);
+    const int rr = SWZ ? swz8_slot(4 * (b >> 1) + (s >> 2)) : 4 * (b >> 1) + (s >> 2);
     const T* a = X + (r0 + 16 * q + rr) * P + c0 + 16 * (b & 1) + 4 * (s & 3);
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
@@ -56,19 +56,6 @@ __device__ __forceinline__ typename TR::frag ld_col(const typename TR::T* X, int
   } else {
     return X[(r0 + acc_row(q, lane >> 5)) * P + c0 + (lane & 31)];
   }
-}
-
-// Row fragment in the same contraction order as ld_col / a fed-back
-// accumulator: columns col0 + 16q + {4g..4g+3, 8+4g..8+4g+3} (16-bit) or
-// col0 + acc_row(q, g) (fp32) of one row. Pair it with ld_col operands.
-template <typename TR>
-__device__ __forceinline__ typename TR::frag ld_row_fed(const typename TR::T* X, int P, int row, int col0, int q) {
-  const int g = (threadIdx.x & 63) >> 5;
-  const typename TR::T* r = X + row * P + col0;
-  if constexpr (TR::E == 8)
-    return TR::ld2x4(r + 16 * q + 4 * g, r + 16 * q + 8 + 4 * g);
-  else
-    return r[acc_row(q, g)];
 }
 
 // Pitches (elements) of row-major tiles. 16-bit: +8 keeps rows 16-byte
@@ -163,56 +150,6 @@ struct RowTile {
           d[1] = s[1];
           d[2] = s[2];
           d[3] = s[3];
-        }
-      }
-    }
-  }
-};
-
-// A ROWS x COLS tile of a row-major matrix (row stride ld elements),
-// prefetched into registers by all NT threads (16-byte chunks) and committed
-// to a row-major LDS tile. Rows >= nrows and columns >= ncols load as zero
-// (ncols and the column offset are multiples of 16 bytes).
-template <typename T, int ROWS, int COLS, int NT>
-struct Tile2D {
-  static constexpr int CH = 16 / int(sizeof(T));
-  static constexpr int NC = COLS / CH;
-  static constexpr int CHUNKS = ROWS * NC;
-  static constexpr int PER = (CHUNKS + NT - 1) / NT;
-  uint4 r[PER];
-
-  static __device__ __forceinline__ int row_of(int u) {
-    const int it = threadIdx.x + u * NT;
-    return it < CHUNKS ? it / NC : ROWS;
-  }
-  static __device__ __forceinline__ int col_of(int u) { return ((threadIdx.x + u * NT) % NC) * CH; }
-
-  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t ld, int64_t row0, int64_t nrows, int col0,
-                                       int ncols) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int row = row_of(u), c = col_of(u);
-      r[u] = make_uint4(0, 0, 0, 0);
-      if (row < ROWS && row0 + row < nrows && col0 + c < ncols)
-        r[u] = *reinterpret_cast<const uint4*>(src + (row0 + row) * ld + col0 + c);
-    }
-  }
-  template <int P>
-  __device__ __forceinline__ void store(T* __restrict__ lds) const {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int row = row_of(u);
-      if (row < ROWS) {
-        const int off = row * P + col_of(u);
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint4*>(lds + off) = r[u];
-        } else {
-          float* d = reinterpret_cast<float*>(lds) + off;
-          const float* f = reinterpret_cast<const float*>(&r[u]);
-          d[0] = f[0];
-          d[1] = f[1];
-          d[2] = f[2];
-          d[3] = f[3];
         }
       }
     }
