@@ -148,24 +148,39 @@ __global__ __launch_bounds__(256) void dw_kernel(Params p) {
 }
 
 // Fixed-order sum of the chunk partials: out[h][r][d] = s * sum_c part[c].
+// A thread sums 4 consecutive elements (one 16-byte load per chunk; D is a
+// multiple of 4, so the 4 share a row) with the chunk loop unrolled, so its
+// loads overlap; every element still adds its chunks in index order.
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_kernel(Params p) {
   using TR = Tr<DT>;
   using T = typename TR::T;
   const int64_t per = int64_t(p.R) * p.D;
-  const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   const int64_t total = 2 * int64_t(p.H) * per;
   if (n >= total) return;
   const int64_t which = n / (int64_t(p.H) * per);
   const int64_t rest = n % (int64_t(p.H) * per);
   const int64_t h = rest / per, e = rest % per;
-  const float* part = p.part + (which * p.H + h) * p.nchunk * per + e;
-  float s = 0.f;
-  for (int c = 0; c < p.nchunk; ++c) s += part[c * per];
+  const float4* part = reinterpret_cast<const float4*>(p.part + (which * p.H + h) * p.nchunk * per + e);
+  const int64_t per4 = per / 4;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < p.nchunk; ++c) {
+    const float4 v = part[c * per4];
+    s0 += v.x;
+    s1 += v.y;
+    s2 += v.z;
+    s3 += v.w;
+  }
   T* out = (T*)(which ? p.dqr : p.dkr);
   // dq_r of the shared P2C convention was accumulated in reversed row order
   const int64_t e_out = (which && p.p2c_shared) ? (int64_t(p.R - 1) - e / p.D) * p.D + e % p.D : e;
-  out[h * per + e_out] = TR::from_f(s * p.scale);
+  T* o = out + h * per + e_out;
+  o[0] = TR::from_f(s0 * p.scale);
+  o[1] = TR::from_f(s1 * p.scale);
+  o[2] = TR::from_f(s2 * p.scale);
+  o[3] = TR::from_f(s3 * p.scale);
 }
 
 template <int DT, int D>
@@ -176,8 +191,8 @@ void launch_dw_d(const Params& p, hipStream_t st) {
 
 template <int DT>
 void launch_sum_dt(const Params& p, hipStream_t st) {
-  const int64_t total = 2 * int64_t(p.H) * p.R * p.D;
-  reduce_kernel<DT><<<unsigned((total + 255) / 256), 256, 0, st>>>(p);
+  const int64_t total = 2 * int64_t(p.H) * p.R * p.D;  // a multiple of 4 (D is)
+  reduce_kernel<DT><<<unsigned((total / 4 + 255) / 256), 256, 0, st>>>(p);
 }
 
 #define DF_DISPATCH(FN, p, st)                     \
